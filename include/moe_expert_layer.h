@@ -1,0 +1,159 @@
+/*
+ * moe_expert_layer.h — C ABI of the MI355X (gfx950) MoE expert-layer library.
+ *
+ * One call of the layer runs, on one GPU's share of the experts:
+ *   route    top-k of each token's routing logits + softmax weights over the k chosen
+ *   permute  group the local (token, slot) pairs by local expert, stable by slot id
+ *   FC1      gate/up grouped GEMM, FP8 E4M3 activations (1x128 UE8M0 scales) against
+ *            FP8 E4M3 weights (128x128 UE8M0 scales) or MXFP4 weights (E2M1, UE8M0 per 32)
+ *   act      SwiGLU or parameterised OAI-SwiGLU (clamp, sigmoid alpha, up bias)
+ *   requant  the intermediate to FP8 E4M3 with one UE8M0 scale per 1x128 block
+ *   FC2      down-projection grouped GEMM
+ *   combine  top-k weighted sum back into token order (no atomics, fixed slot order)
+ *
+ * Sources: the fused "Mega MoE" expert layer as described by DeepGEMM PR #445
+ * ("fix(sm90): support parameterized SwiGLU in FP8 MegaMoE": Summary, Changes,
+ * Compatibility), DeepGEMM PR #386 ("... native UE8M0, and direct combine":
+ * description), FlashInfer's "Pull Style Cutedsl Megakernel" (Layout: FC1/FC2 fused
+ * scheduling and a top-k reduce), and TensorRT-LLM PR #16346 ("DSV4 o_proj: fuse
+ * fp8/UE8M0 quantize ...": Description, 1x128 UE8M0 requant with an amax per block).
+ *
+ * Conventions for every entry point
+ *   - Memory: every tensor pointer is a device pointer owned by the caller; the
+ *     library never allocates, frees or keeps pointers after a call returns.  The
+ *     workspace (scratch) is caller-owned device memory of at least
+ *     moe_workspace_size() bytes, 256-byte aligned; its contents on entry are
+ *     ignored (every counter the kernels use is initialised inside the call).
+ *   - Layouts are row-major and dense:
+ *       logits      float32 [T, E_tot]
+ *       x           E4M3 bytes [T, H]            x_sf   UE8M0 bytes [T, H/128]
+ *       w1 (fp8)    E4M3 bytes [E_loc, 2I, H]    w1_sf  UE8M0 [E_loc, 2I/128, H/128]
+ *       w1 (mxfp4)  E2M1 pairs [E_loc, 2I, H/2]  w1_sf  UE8M0 [E_loc, 2I, H/32]
+ *       w2 (fp8)    E4M3 bytes [E_loc, H, I]     w2_sf  UE8M0 [E_loc, H/128, I/128]
+ *       w2 (mxfp4)  E2M1 pairs [E_loc, H, I/2]   w2_sf  UE8M0 [E_loc, H, I/32]
+ *     W1 rows [0, I) are the gate projection and rows [I, 2I) the up projection.
+ *     MXFP4: element 2i of a K-row is the low nibble of byte i.  E4M3 is OCP E4M3FN.
+ *     UE8M0 byte b is 2^(b-127); 255 (NaN) is not allowed.
+ *       topk_ids    int32 [T, k]  slot j = j-th largest logit (ties: lower expert id)
+ *       topk_w      float32 [T, k] softmax over the k chosen logits (computed in fp64)
+ *       counts      int32 [E_loc]   rows per local expert
+ *       offsets     int32 [E_loc+1] exclusive scan of counts; offsets[E_loc] = R
+ *       row_to_slot int32 [T*k]  rows [0, R) hold slot ids s = t*k + j, rest -1
+ *       slot_to_row int32 [T*k]  row of slot s, or -1 when expert ids[s] is not local
+ *       h           E4M3 bytes [T*k, I] (rows [0, R) written), h_sf UE8M0 [T*k, I/128]
+ *       y           bfloat16 bits [T, H]; tokens with no local slot get +0
+ *   - Requant rule: per 1x128 block, scale 2^e with the smallest integer e such that
+ *     448 * 2^e >= amax (byte 127 for an all-zero block), codes = E4M3 round to
+ *     nearest even of h * 2^-e.
+ *   - Logits must be finite; non-finite logits give unspecified routing.
+ *   - Validation happens on the host before any launch; on error nothing is
+ *     launched and a moe_status is returned (moe_last_error() has details).  A
+ *     call with num_tokens = 0 returns MOE_OK without launching anything or
+ *     touching any buffer.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream),
+ *     do no host synchronisation and no allocation, so they may be captured in a
+ *     HIP graph.  Calls on distinct workspaces may run concurrently.
+ *   - Alignment: x, x_sf, w1, w2, h, logits, y and the workspace must be 16-byte
+ *     aligned (the workspace 256-byte aligned).
+ *   - Limits: H and I multiples of 128; 1 <= E_loc <= E_tot <= 1024;
+ *     1 <= k <= min(E_tot, 16); T*k < 2^31.
+ */
+#ifndef MOE_EXPERT_LAYER_H_
+#define MOE_EXPERT_LAYER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,          /* a required pointer is NULL */
+  MOE_ERR_INVALID_DESC = 2,  /* a size or parameter in the descriptor is out of range */
+  MOE_ERR_MISALIGNED = 3,    /* a pointer violates the alignment rules above */
+  MOE_ERR_UNSUPPORTED = 4,   /* valid request this build cannot run (e.g. not a gfx950 device) */
+  MOE_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than moe_workspace_size() */
+  MOE_ERR_DEVICE = 6         /* a HIP runtime call or launch failed */
+} moe_status;
+
+/* Activation names follow the pages' API: "swiglu" and "swigluoai". */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
+
+/* Weight formats: FP8 E4M3 with 128x128 UE8M0 block scales, or MXFP4 (E2M1, UE8M0 per 32 along K). */
+typedef enum { MOE_W_FP8_E4M3_B128 = 0, MOE_W_MXFP4_E2M1_B32 = 1 } moe_wfmt;
+
+typedef struct {
+  int32_t num_tokens;     /* T >= 0 */
+  int32_t hidden;         /* H, multiple of 128 */
+  int32_t inter;          /* I, multiple of 128 */
+  int32_t num_experts;    /* E_tot: routing width */
+  int32_t local_begin;    /* e0: first local expert */
+  int32_t num_local;      /* E_loc: local experts are [e0, e0 + E_loc) */
+  int32_t topk;           /* k */
+  int32_t weight_format;  /* moe_wfmt */
+  int32_t activation;     /* moe_act */
+  float act_clamp;        /* OAI only: gate <= clamp, |up| <= clamp; +inf = no clamp (must be > 0) */
+  float act_alpha;        /* OAI only: sigmoid(alpha * gate); default 1.0 */
+  float act_up_bias;      /* OAI only: (up + up_bias); default 0.0 */
+  int32_t variant;        /* -1 = heuristic kernel choice; 0 = general tiles; 1 = small-row tiles */
+} moe_layer_desc;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION at build time). */
+int moe_abi_version(void);
+
+/* Static string naming a status code. */
+const char* moe_status_str(int status);
+
+/* Details of the last error returned on the calling thread ("" when none). */
+const char* moe_last_error(void);
+
+/* Fill *desc with defaults: SwiGLU, FP8 weights, clamp +inf, alpha 1.0, up_bias 0.0,
+ * variant -1, all sizes 0 (the pages' Compatibility section: the OAI parameters
+ * default to the standard SwiGLU behaviour).  Host only. */
+moe_status moe_desc_defaults(moe_layer_desc* desc);
+
+/* Bytes of workspace every entry point below needs for this descriptor.  Host only;
+ * validates the descriptor. */
+moe_status moe_workspace_size(const moe_layer_desc* desc, size_t* bytes);
+
+/* Route + permute: logits -> topk_ids, topk_w, counts, offsets, row_to_slot, slot_to_row.
+ * All outputs are required (caller-owned device buffers of the sizes above). */
+moe_status moe_route_permute(const moe_layer_desc* desc, const float* logits, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, int32_t* offsets, int32_t* row_to_slot,
+                             int32_t* slot_to_row, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* FC1 + activation + 1x128 requant for every row of every local expert.
+ * Reads x/x_sf rows of token row_to_slot[r] / k, writes h/h_sf rows [0, R). */
+moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* desc, const uint8_t* x, const uint8_t* x_sf,
+                                  const uint8_t* w1, const uint8_t* w1_sf, const int32_t* offsets,
+                                  const int32_t* row_to_slot, uint8_t* h, uint8_t* h_sf,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* FC2 + top-k weighted combine into y (bf16 bits, [T, H]).  The fp32 FC2 rows are
+ * kept in the workspace; the sum over a token's local slots runs in slot order
+ * j = 0..k-1 in fp32 and is rounded once to bf16. */
+moe_status moe_grouped_fc2_combine(const moe_layer_desc* desc, const uint8_t* h, const uint8_t* h_sf,
+                                   const uint8_t* w2, const uint8_t* w2_sf, const int32_t* offsets,
+                                   const int32_t* row_to_slot, const int32_t* slot_to_row,
+                                   const float* topk_w, uint16_t* y, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* The whole layer.  The opt_* outputs may be NULL (then they live in the workspace);
+ * when given they receive the routing/grouping results. */
+moe_status moe_layer(const moe_layer_desc* desc, const float* logits, const uint8_t* x,
+                     const uint8_t* x_sf, const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2,
+                     const uint8_t* w2_sf, uint16_t* y, int32_t* opt_topk_ids, float* opt_topk_w,
+                     int32_t* opt_counts, int32_t* opt_offsets, int32_t* opt_row_to_slot,
+                     int32_t* opt_slot_to_row, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXPERT_LAYER_H_ */

@@ -1,0 +1,41 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopk = 16;
+constexpr int kPermChunk = 4096;  // slots per permute workgroup
+
+struct Shape {
+  int T, H, I, E, e0, EL, k;
+  int wfmt;  // 0 fp8 block-128, 1 mxfp4
+  int act;   // 0 swiglu, 1 oai
+  float clamp, alpha, bias;
+};
+
+// route + permute ----------------------------------------------------------
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+// buckets: EL local experts + 1 trailing bucket for non-local slots
+hipError_t launch_permute(const int32_t* ids, int nslots, int e0, int EL, int32_t* chunk_cnt, int32_t* chunk_base,
+                          int32_t* counts, int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row,
+                          hipStream_t s);
+
+// grouped GEMMs ------------------------------------------------------------
+// Tile plan: plan[e] = first m-tile of local expert e, plan[EL] = number of m-tiles.
+int gemm_block_m(int variant);
+size_t gemm_max_mtiles(int rows_cap, int EL, int variant);
+hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
+                      const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
+                      uint8_t* h_sf, int32_t* plan, hipStream_t s);
+hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
+                      const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, hipStream_t s);
+
+// combine --------------------------------------------------------------------
+hipError_t launch_combine(const float* y2, const int32_t* slot_to_row, const float* topk_w, int T, int H, int k,
+                          uint16_t* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before touching a GPU (no compute calls here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from moe_expert_layer_amd import binding as B
+from moe_expert_layer_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return B.lib()
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_abi_version() == 1
+    assert B.status_str(0) == "MOE_OK" and B.status_str(5) == "MOE_ERR_WORKSPACE"
+    assert B.status_str(99) == "MOE_STATUS_UNKNOWN"
+
+
+def test_defaults_follow_standard_swiglu(L):
+    d = B.MoeLayerDesc()
+    assert L.moe_desc_defaults(ctypes.byref(d)) == 0
+    assert d.activation == B.MOE_ACT_SWIGLU and d.weight_format == B.MOE_W_FP8_E4M3_B128
+    assert math.isinf(d.act_clamp) and d.act_alpha == 1.0 and d.act_up_bias == 0.0 and d.variant == -1
+
+
+@pytest.mark.parametrize("i", range(5))
+def test_workspace_size_covers_capacity(L, i):
+    w = synth.workload(i)
+    n = B.moe_workspace_size(B.desc_from_workload(w))
+    cap = w.tokens * w.topk
+    assert n >= cap * (w.hidden * 4 + w.inter + w.inter // 128 + 16)
+    assert n % 256 == 0
+
+
+@pytest.mark.parametrize("field,value", [("hidden", 100), ("inter", 0), ("num_experts", 0), ("num_experts", 2000),
+                                         ("topk", 0), ("topk", 17), ("num_local", 0), ("local_begin", -1),
+                                         ("num_tokens", -5), ("weight_format", 7), ("activation", 3),
+                                         ("variant", 5)])
+def test_invalid_descriptor_rejected(L, field, value):
+    d = B.desc_from_workload(synth.workload("tiny"))
+    setattr(d, field, value)
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_INVALID_DESC
+    assert L.moe_last_error()
+
+
+def test_local_range_must_fit(L):
+    d = B.desc_from_workload(synth.workload("decode"))
+    d.local_begin = 240  # 240 + 32 > 256
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_INVALID_DESC
+
+
+def test_oai_parameters_validated(L):
+    d = B.desc_from_workload(synth.workload("oai"))
+    n = ctypes.c_size_t(0)
+    d.act_clamp = 0.0
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_INVALID_DESC
+    d.act_clamp, d.act_alpha = 7.0, float("nan")
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_INVALID_DESC
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch(L):
+    d = B.desc_from_workload(synth.workload("tiny"))
+    P = ctypes.c_void_p
+    # NULL inputs
+    st = L.moe_layer(ctypes.byref(d), *([None] * 15), 0, None)
+    assert st == B.MOE_ERR_NULL
+    # misaligned inputs (never dereferenced: validation fails first)
+    bad = [P(0x1001)] * 8 + [None] * 6
+    st = L.moe_layer(ctypes.byref(d), *bad, P(0x100000), 1 << 30, None)
+    assert st == B.MOE_ERR_MISALIGNED
+    # small workspace
+    good = [P(0x10000)] * 8 + [None] * 6
+    st = L.moe_layer(ctypes.byref(d), *good, P(0x100000), 16, None)
+    assert st == B.MOE_ERR_WORKSPACE
+    st = L.moe_layer(ctypes.byref(d), *good, P(0x100010), 1 << 30, None)
+    assert st == B.MOE_ERR_MISALIGNED  # workspace must be 256-byte aligned
+
+
+def test_zero_tokens_is_a_noop_without_device(L):
+    d = B.desc_from_workload(synth.shrink(synth.workload("tiny"), tokens=0))
+    assert L.moe_layer(ctypes.byref(d), *([None] * 15), 0, None) == B.MOE_OK
+    assert L.moe_route_permute(ctypes.byref(d), *([None] * 7), None, 0, None) == B.MOE_OK
