@@ -1,4 +1,4 @@
-// Grouped expert GEMMs on gfx950 scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4).
+// Grouped expert GEMMs on gfx950 scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).
 //
 // FC1: for every row r of local expert e (token t = row_to_slot[r] / k)
 //        g = x_t . W1[e, n],  u = x_t . W1[e, I + n]   (FP8 E4M3 x with 1x128 UE8M0 scales,
@@ -13,22 +13,25 @@
 // into o_a proj" (Description: FP8 + 1x128 UE8M0 emitted from the GEMM epilogue with
 // an amax reduction per block).
 //
-// Scales are applied by the MFMA itself: each 16x16x128 instruction covers exactly one
-// 128-wide K block, so the activation scale is one byte per row and the FP8 weight
-// scale one byte per 128-row block; MXFP4 weights carry one byte per (row, 32-K block).
+// The MFMA applies the scales: a 128-wide K step is two 32x32x64 instructions that share
+// one activation scale per row and one FP8 weight scale per 128-row block; MXFP4 weights
+// carry one scale per (row, 32-wide K block).
 //
-// Operand layout of the scaled MFMA (measured on gfx950): lane l works on row/column
-// l%16; an FP8 operand holds K bytes [16*(l/16), +16) and [64 + 16*(l/16), +16) of the
-// 128-wide block; an FP4 operand holds K elements [32*(l/16), +32) (element 2i in the
-// low nibble of byte i); the scale byte of lane l covers row/column l%16 and the
-// 32-wide K block l/16; the result lane l holds rows 4*(l/16)+i, column l%16.
+// Operand layout of the scaled 32x32x64 MFMA (measured on gfx950): lane l works on
+// row/column l%32 and K half-block kb = l/32 of the 64-wide K block; an FP8 operand holds
+// K bytes [16kb, +16) and [32 + 16kb, +16); an FP4 operand holds K elements [32kb, +32)
+// (element 2i in the low nibble of byte i); lane l's scale byte covers row/column l%32
+// and the 32-wide K block kb; result lane l holds rows 8*(i/4) + 4*(l/32) + i%4, column l%32.
 //
-// Tiles: 128 rows x 256 weight rows (FC1: 128 gate + the matching 128 up rows, i.e. one
-// 1x128 requant block of h; FC2: 256 output columns), 4 waves in 2x2, each wave 64 rows
-// x 8 column tiles of 16.  K advances 128 per step through one LDS buffer with the
-// next step prefetched into registers.  LDS rows are 16-byte-chunk XOR swizzled so the
-// MFMA operand reads are bank-conflict free.  Workgroups map to tiles through an
-// XCD-aware order (consecutive tiles of one expert run on one XCD and share its L2).
+// Tiles: 128 rows x BN weight rows (FC1: BN = 256 = 128 gate + the matching 128 up rows,
+// i.e. exactly one 1x128 requant block of h; FC2: BN output columns), 4 waves in 2x2.
+// K advances 128 per stage through a ring of NSTAGE LDS stages filled by direct
+// global->LDS loads (global_load_lds_dwordx4): NSTAGE-1 stages are in flight while one is
+// consumed, and the loads take no registers.  The waits are explicit (s_waitcnt vmcnt +
+// s_barrier).  LDS rows are 16-byte-chunk XOR swizzled so the operand reads are bank
+// conflict free.  Workgroups map to tiles in an XCD-aware order (consecutive tiles of one
+// expert on one XCD, sharing its L2).  Row tiles past an expert's last row skip their
+// MFMAs (decode-sized experts).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -37,10 +40,12 @@
 
 namespace moe {
 
-constexpr int kBM = 128;   // rows per tile
-constexpr int kBN = 256;   // weight rows per tile
-constexpr int kBK = 128;   // K per step
-constexpr int kGroupN = 8; // n-tiles per group in the tile order
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128;       // rows per tile
+constexpr int kBK = 128;       // K per stage
+constexpr int kGroupN = 8;     // n-tiles per group in the tile order
+constexpr int kMaxKSteps = 64; // K <= 8192 (scales of a tile are staged in LDS)
 
 struct GemmArgs {
   const uint8_t* A;      // FC1: x [T, K]; FC2: h [cap, K]
@@ -65,9 +70,47 @@ struct GemmArgs {
   float clamp, alpha, bias;
 };
 
+template <int MODE, int WFMT, int BN>
+struct Cfg {
+  static constexpr int NSTAGE = (WFMT == 0 && BN == 256) ? 3 : 4;
+  static constexpr int B_ROWB = WFMT == 0 ? 128 : 64;      // weight bytes per row per stage
+  static constexpr int A_BYTES = kBM * 128;                // 16 KB
+  static constexpr int B_BYTES = BN * B_ROWB;
+  static constexpr int S_BYTES = WFMT == 1 ? BN * 4 : 0;   // MXFP4 scale dwords per stage
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int A_DMA = A_BYTES / 1024 / 4;         // 16-byte DMA instructions per wave per stage
+  static constexpr int B_DMA = B_BYTES / 1024 / 4;
+  static constexpr int S_DMA = WFMT == 1 ? S_BYTES / 256 / 4 : 0;  // 4-byte DMA instructions per wave
+  static constexpr int PER_STAGE = A_DMA + B_DMA + S_DMA;
+  static constexpr int NT = BN / 2 / 32;                   // 32-wide column tiles per wave
+  static constexpr int A_ROWS_PER_KB = 1024 / 128;         // rows per 1 KB DMA block
+  static constexpr int B_ROWS_PER_KB = 1024 / B_ROWB;
+};
+
+// ---------------------------------------------------------------------------------------
+// direct global -> LDS loads (the wave writes 64 lanes x 16 bytes at m0, lane order)
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// XOR swizzles of 16-byte chunks: conflict-free for 8 (and 16) consecutive rows read at one chunk
+__device__ __forceinline__ int g8(int r) { return (r ^ (r >> 3)) & 7; }         // 128-byte rows
+__device__ __forceinline__ int g4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }  // 64-byte rows
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
 __device__ __forceinline__ int find_expert(const int32_t* __restrict__ plan, int EL, int mt) {
-  // last e with plan[e] <= mt  (that expert is non-empty)
-  int lo = 0, hi = EL - 1;
+  int lo = 0, hi = EL - 1;  // last e with plan[e] <= mt (that expert is non-empty)
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (plan[mid] <= mt) lo = mid; else hi = mid - 1;
@@ -75,34 +118,23 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ plan, int
   return lo;
 }
 
-__device__ __forceinline__ uint4 lds_load16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void lds_store16(uint8_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
-__device__ __forceinline__ uint4 gload16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+template <int MODE, int WFMT, int BN>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
+  using C = Cfg<MODE, WFMT, BN>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NSTAGE * C::STAGE];
+  __shared__ uint8_t s_asf[kMaxKSteps * kBM];  // [ks][row] activation scales
+  __shared__ uint8_t s_bsf[2 * kMaxKSteps];    // [block][ks] FP8 weight scales
+  __shared__ int s_tok[kBM];
+  __shared__ float s_amax[2][kBM];
 
-// Swizzled byte offset of 16-byte chunk c of row r in a [rows][128 B] tile.
-__device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
-// Swizzled byte offset of 16-byte chunk c of row r in a [rows][64 B] tile.
-__device__ __forceinline__ int sw64(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
-
-template <int MODE, int WFMT>  // MODE 1 = FC1, 2 = FC2; WFMT 0 = fp8 block-128, 1 = mxfp4
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs g) {
-  constexpr int B_ROWB = WFMT == 0 ? 128 : 64;  // bytes of one weight row per K step
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBN * B_ROWB];
-  __shared__ int lds_bsf[WFMT == 1 ? kBN : 1];
-  __shared__ float lds_amax[2][kBM];
-
-  const int total_m = g.plan[g.EL];
-  const int total = total_m * g.n_tiles;
+  const int total = g.plan[g.EL] * g.n_tiles;
   const int bid = blockIdx.x;
   if (bid >= total) return;
-  // XCD-aware order: dispatch is round-robin over 8 XCDs, give each XCD a contiguous range.
-  int L;
+  int L;  // XCD-aware order: dispatch is round-robin over 8 XCDs; each XCD gets a contiguous range
   {
     const int x = bid & 7, p = bid >> 3, q = total >> 3, r = total & 7;
     L = x * q + (x < r ? x : r) + p;
   }
-  // expert-major order: tiles of expert e are [plan[e]*NT, plan[e+1]*NT)
   const int e = find_expert(g.plan, g.EL, L / g.n_tiles);
   const int mt_e = g.plan[e + 1] - g.plan[e];
   const int li = L - g.plan[e] * g.n_tiles;
@@ -112,171 +144,185 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs g) {
   const int idx = li - grp * gn * mt_e;
   const int m_tile = idx / gsz;
   const int n_tile = grp * gn + idx % gsz;
-
   const int row_begin = g.offsets[e] + m_tile * kBM;
   const int rows = min(kBM, g.offsets[e + 1] - row_begin);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int ksteps = g.K / kBK;
+  const int nk = g.K / kBK;
+  const int n0 = MODE == 1 ? n_tile * 128 : n_tile * BN;
 
-  // ---- global source pointers for this thread's share of the tile loads ----
-  // A: chunk q = tid + 256 j -> row (tid >> 3) + 32 j, chunk tid & 7
-  const uint8_t* a_src[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int r = (tid >> 3) + 32 * j;
-    if (r >= rows) r = 0;
-    const int grow = row_begin + r;
-    long long arow;
-    if (MODE == 1) arow = g.row_to_slot[grow] / g.k; else arow = grow;
-    a_src[j] = g.A + arow * (long long)g.K + ((tid & 7) << 4);
+  // ---- A row sources (token rows for FC1) and scales staged in LDS ----
+  if (tid < kBM) {
+    const int r = tid < rows ? tid : 0;
+    s_tok[tid] = MODE == 1 ? g.row_to_slot[row_begin + r] / g.k : row_begin + r;
   }
-  // B rows of the tile: FC1 local n < 128 -> gate row n0 + n, else up row I + n0 + n - 128
-  const uint8_t* b_exp = g.B + (long long)e * g.b_estride;
-  const int n0 = MODE == 1 ? n_tile * 128 : n_tile * kBN;
+  __syncthreads();
+  for (int i = tid; i < nk * kBM; i += 256) {
+    const int ks = i / kBM, r = i - ks * kBM;
+    s_asf[i] = g.A_sf[(long long)s_tok[r] * nk + ks];
+  }
+  const uint8_t* bsf_e = g.B_sf + (long long)e * g.bsf_estride;
+  if (WFMT == 0) {
+    // block rows: FC1 gate n0/128 and up (I+n0)/128; FC2 n0/128 and n0/128 + 1 (clamped)
+    for (int i = tid; i < 2 * nk; i += 256) {
+      const int blk = i / nk, ks = i - blk * nk;
+      int br;
+      if (MODE == 1) br = blk == 0 ? n0 / 128 : (g.I + n0) / 128;
+      else br = min(n0 / 128 + blk, g.N / 128 - 1);
+      s_bsf[i] = bsf_e[(long long)br * nk + ks];
+    }
+  }
+
+  // ---- DMA sources of this lane, with the swizzled chunk folded in ----
+  const uint8_t* a_src[C::A_DMA];
+#pragma unroll
+  for (int j = 0; j < C::A_DMA; ++j) {
+    const int r = (wave * C::A_DMA + j) * C::A_ROWS_PER_KB + (lane >> 3);
+    const int c = (lane & 7) ^ g8(r);
+    a_src[j] = g.A + (long long)s_tok[r] * g.K + c * 16;
+  }
+  const uint8_t* b_e = g.B + (long long)e * g.b_estride;
   auto b_row = [&](int n) -> int {
     if (MODE == 1) return n < 128 ? n0 + n : g.I + n0 + (n - 128);
     const int rr = n0 + n;
     return rr < g.N ? rr : g.N - 1;
   };
-  constexpr int NBL = WFMT == 0 ? 8 : 4;  // 16-byte B loads per thread per step
-  const uint8_t* b_src[NBL];
+  const uint8_t* b_src[C::B_DMA];
 #pragma unroll
-  for (int j = 0; j < NBL; ++j) {
+  for (int j = 0; j < C::B_DMA; ++j) {
     if (WFMT == 0) {
-      const int n = (tid >> 3) + 32 * j;
-      b_src[j] = b_exp + (long long)b_row(n) * g.K + ((tid & 7) << 4);
+      const int n = (wave * C::B_DMA + j) * C::B_ROWS_PER_KB + (lane >> 3);
+      const int c = (lane & 7) ^ g8(n);
+      b_src[j] = b_e + (long long)b_row(n) * g.K + c * 16;
     } else {
-      const int n = (tid >> 2) + 64 * j;
-      b_src[j] = b_exp + (long long)b_row(n) * (g.K / 2) + ((tid & 3) << 4);
+      const int n = (wave * C::B_DMA + j) * C::B_ROWS_PER_KB + (lane >> 2);
+      const int c = (lane & 3) ^ g4(n);
+      b_src[j] = b_e + (long long)b_row(n) * (g.K / 2) + c * 16;
     }
   }
-  const uint8_t* bsf_exp = g.B_sf + (long long)e * g.bsf_estride;
-  // mxfp4 scales: thread tid owns weight row tid of the tile (4 bytes per K step)
-  const uint8_t* bsf_src = WFMT == 1 ? bsf_exp + (long long)b_row(tid) * (g.K / 32) : nullptr;
+  const uint8_t* s_src = nullptr;  // MXFP4: lane owns weight row wave*64 + lane (4 scale bytes per stage)
+  if (WFMT == 1) s_src = bsf_e + (long long)b_row(wave * 64 + lane) * (g.K / 32);
 
-  // ---- MFMA operand rows owned by this lane ----
-  const int lrow = lane & 15, kb = lane >> 4;
-  const uint8_t* a_sf_row[4];
+  const uint32_t ring0 = lds_addr(ring);
+  auto issue = [&](int ks) {
+    const uint32_t st = ring0 + (uint32_t)((ks % C::NSTAGE) * C::STAGE);
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    int r = wm * 64 + mi * 16 + lrow;
-    if (r >= rows) r = 0;
-    const int grow = row_begin + r;
-    long long arow;
-    if (MODE == 1) arow = g.row_to_slot[grow] / g.k; else arow = grow;
-    a_sf_row[mi] = g.A_sf + arow * (long long)ksteps;
-  }
-  auto bcol = [&](int ct) -> int {  // first weight row (tile-local) of column tile ct for this wave
-    if (MODE == 1) return ct < 4 ? wn * 64 + ct * 16 : 128 + wn * 64 + (ct - 4) * 16;
-    return wn * 128 + ct * 16;
-  };
-  // fp8 weight-scale block rows of this wave (uniform): FC1 gate/up, FC2 one block
-  int sfb0, sfb1;
-  if (MODE == 1) { sfb0 = n0 / 128; sfb1 = (g.I + n0) / 128; }
-  else { sfb0 = min((n0 + wn * 128) / 128, g.N / 128 - 1); sfb1 = sfb0; }
-
-  v4f acc[4][8];
+    for (int j = 0; j < C::A_DMA; ++j)
+      dma16(a_src[j] + ks * kBK, uniform(st + (wave * C::A_DMA + j) * 1024));
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) acc[mi][ct] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  uint4 pa[4], pb[NBL];
-  int pbsf = 0;
-  auto gload_step = [&](int ks) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pa[j] = gload16(a_src[j] + ks * kBK);
-#pragma unroll
-    for (int j = 0; j < NBL; ++j) pb[j] = gload16(b_src[j] + ks * (WFMT == 0 ? kBK : kBK / 2));
-    if (WFMT == 1) pbsf = *reinterpret_cast<const int*>(bsf_src + ks * 4);
-  };
-  auto lds_store_step = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds_store16(lds_a + sw128((tid >> 3) + 32 * j, tid & 7), pa[j]);
-#pragma unroll
-    for (int j = 0; j < NBL; ++j) {
-      if (WFMT == 0) lds_store16(lds_b + sw128((tid >> 3) + 32 * j, tid & 7), pb[j]);
-      else lds_store16(lds_b + sw64((tid >> 2) + 64 * j, tid & 3), pb[j]);
-    }
-    if (WFMT == 1) lds_bsf[tid] = pbsf;
+    for (int j = 0; j < C::B_DMA; ++j)
+      dma16(b_src[j] + ks * (WFMT == 0 ? kBK : kBK / 2), uniform(st + C::A_BYTES + (wave * C::B_DMA + j) * 1024));
+    if (WFMT == 1) dma4(s_src + ks * 4, uniform(st + C::A_BYTES + C::B_BYTES + wave * 256));
   };
 
-  gload_step(0);
-  for (int ks = 0; ks < ksteps; ++ks) {
-    __syncthreads();  // previous step's LDS reads are done
-    lds_store_step();
-    __syncthreads();
-    if (ks + 1 < ksteps) gload_step(ks + 1);
+  v16f acc[2][C::NT];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ct = 0; ct < C::NT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mi][ct][i] = 0.f;
 
-    int sa[4];
+  const int lrow = lane & 31, kb = lane >> 5;
+  bool mi_live[2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) sa[mi] = a_sf_row[mi][ks];
-    v8i af[4];
+  for (int mi = 0; mi < 2; ++mi) mi_live[mi] = wm * 64 + mi * 32 < rows;
+  // first weight row (tile-local) of column tile ct of this wave
+  auto bcol = [&](int ct) -> int {
+    if (MODE == 1) return ct < C::NT / 2 ? wn * 64 + ct * 32 : 128 + wn * 64 + (ct - C::NT / 2) * 32;
+    return wn * (BN / 2) + ct * 32;
+  };
+
+  // prologue: NSTAGE-1 stages in flight
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int r = wm * 64 + mi * 16 + lrow;
-      const uint4 lo = lds_load16(lds_a + sw128(r, kb));
-      const uint4 hi = lds_load16(lds_a + sw128(r, kb + 4));
-      af[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+  for (int s = 0; s < C::NSTAGE - 1; ++s)
+    if (s < nk) issue(s);
+
+  for (int ks = 0; ks < nk; ++ks) {
+    const int rem = nk - 1 - ks;
+    if (C::NSTAGE == 4 && rem >= 2) wait_vm_barrier<2 * C::PER_STAGE>();
+    else if (rem >= 1) wait_vm_barrier<C::PER_STAGE>();
+    else wait_vm_barrier<0>();
+    if (ks + C::NSTAGE - 1 < nk) issue(ks + C::NSTAGE - 1);
+
+    const uint8_t* st = ring + (ks % C::NSTAGE) * C::STAGE;
+    const uint8_t* sa_ = st;
+    const uint8_t* sb_ = st + C::A_BYTES;
+    int sa[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) sa[mi] = s_asf[ks * kBM + wm * 64 + mi * 32 + lrow];
     int sbu0 = 0, sbu1 = 0;
     if (WFMT == 0) {
-      sbu0 = bsf_exp[(long long)sfb0 * ksteps + ks];
-      sbu1 = bsf_exp[(long long)sfb1 * ksteps + ks];
+      if (MODE == 1) { sbu0 = s_bsf[ks]; sbu1 = s_bsf[nk + ks]; }
+      else { sbu0 = s_bsf[(BN == 256 ? wn : 0) * nk + ks]; sbu1 = sbu0; }
     }
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const int n = bcol(ct) + lrow;
-      v8i bf;
-      int sb;
-      if (WFMT == 0) {
-        const uint4 lo = lds_load16(lds_b + sw128(n, kb));
-        const uint4 hi = lds_load16(lds_b + sw128(n, kb + 4));
-        bf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        sb = (MODE == 1 && ct >= 4) ? sbu1 : sbu0;
-      } else {
-        const uint4 q = lds_load16(lds_b + sw64(n, kb));
-        bf = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-        sb = (lds_bsf[n] >> (8 * kb)) & 0xff;
+    for (int h = 0; h < 2; ++h) {
+      v8i af[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int r = wm * 64 + mi * 32 + lrow;
+        const uint4 lo = lds16(sa_ + r * 128 + (((4 * h + kb) ^ g8(r)) << 4));
+        const uint4 hi = lds16(sa_ + r * 128 + (((4 * h + 2 + kb) ^ g8(r)) << 4));
+        af[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        acc[mi][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf, acc[mi][ct], 0, WFMT == 0 ? 0 : 4,
-                                                                       0, sa[mi], 0, sb);
+      for (int ct = 0; ct < C::NT; ++ct) {
+        const int n = bcol(ct) + lrow;
+        v8i bf;
+        int sb;
+        if (WFMT == 0) {
+          const uint4 lo = lds16(sb_ + n * 128 + (((4 * h + kb) ^ g8(n)) << 4));
+          const uint4 hi = lds16(sb_ + n * 128 + (((4 * h + 2 + kb) ^ g8(n)) << 4));
+          bf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sb = (MODE == 1 && ct >= C::NT / 2) ? sbu1 : sbu0;
+        } else {
+          const uint4 q = lds16(sb_ + n * 64 + (((2 * h + kb) ^ g4(n)) << 4));
+          bf = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          const int dw = *reinterpret_cast<const int*>(st + C::A_BYTES + C::B_BYTES + n * 4);
+          sb = (dw >> (8 * (2 * h + kb))) & 0xff;
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          if (mi_live[mi])
+            acc[mi][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf, acc[mi][ct], 0,
+                                                                          WFMT == 0 ? 0 : 4, 0, sa[mi], 0, sb);
+      }
     }
   }
 
   if (MODE == 2) {
-    // ---- FC2 epilogue: fp32 rows of Y2 ----
+    // ---- FC2 epilogue: fp32 rows of Y2 (32 consecutive columns per lane group) ----
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi) {
+      if (!mi_live[mi]) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + mi * 16 + 4 * kb + i;
+      for (int i = 0; i < 16; ++i) {
+        const int r = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
         if (r < rows) {
           float* dst = g.y2 + (long long)(row_begin + r) * g.N;
 #pragma unroll
-          for (int ct = 0; ct < 8; ++ct) {
+          for (int ct = 0; ct < C::NT; ++ct) {
             const int col = n0 + bcol(ct) + lrow;
             if (col < g.N) dst[col] = acc[mi][ct][i];
           }
         }
       }
+    }
     return;
   }
 
   // ---- FC1 epilogue: activation, 1x128 amax, UE8M0 scale, E4M3 codes ----
-  // lane holds, for rows 4*kb+i of each row tile, h columns wn*64 + c*16 + lrow (c = 0..3)
-  float hv[4][4][4];
+  // lane holds rows 8*(i/4) + 4*kb + i%4 of each row tile; h column wn*64 + c*32 + lrow (c = 0, 1)
+  constexpr int NC = C::NT / 2;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float gt = acc[mi][c][i], up = acc[mi][c + 4][i];
+      for (int i = 0; i < 16; ++i) {
+        float gt = acc[mi][c][i], up = acc[mi][c + NC][i];
         float hh;
         if (g.act == 1) {
           gt = fminf(gt, g.clamp);
@@ -285,50 +331,43 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs g) {
         } else {
           hh = gt * sigmoidf_(gt) * up;
         }
-        hv[mi][c][i] = hh;
+        acc[mi][c][i] = hh;  // h overwrites the gate accumulator
       }
-  float am[4][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float m = fmaxf(fmaxf(fabsf(hv[mi][0][i]), fabsf(hv[mi][1][i])), fmaxf(fabsf(hv[mi][2][i]), fabsf(hv[mi][3][i])));
+    for (int i = 0; i < 16; ++i) {
+      float m = 0.f;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-      am[mi][i] = m;
+      for (int c = 0; c < NC; ++c) m = fmaxf(m, fabsf(acc[mi][c][i]));
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (lrow == 0) s_amax[wn][wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3)] = m;
     }
-  if (lrow == 0) {
+  __syncthreads();  // every wave is past its last ring read; s_amax complete
+  uint8_t* stage_h = ring;  // [128 rows][128 B] code tile
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_amax[wn][wm * 64 + mi * 16 + 4 * kb + i] = am[mi][i];
-  }
-  __syncthreads();  // also: every wave is past its last LDS operand read
-  uint8_t* lds_h = lds_b;  // [128 rows][128 B] staging of the E4M3 codes
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + mi * 16 + 4 * kb + i;
-      const float amax = fmaxf(lds_amax[0][r], lds_amax[1][r]);
+    for (int i = 0; i < 16; ++i) {
+      const int r = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
+      const float amax = fmaxf(s_amax[0][r], s_amax[1][r]);
       const int byte = ue8m0_for_amax(amax);
       const float inv = inv_scale_of(byte);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(hv[mi][c][i] * inv, 0.0f, 0, false) & 0xff;
-        lds_h[r * 128 + wn * 64 + c * 16 + lrow] = (uint8_t)code;
+      for (int c = 0; c < NC; ++c) {
+        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(acc[mi][c][i] * inv, 0.0f, 0, false) & 0xff;
+        stage_h[r * 128 + wn * 64 + c * 32 + lrow] = (uint8_t)code;
       }
-      if (wn == 0 && lrow == 0 && r < rows)
-        g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = (uint8_t)byte;
+      if (wn == 0 && lrow == 0 && r < rows) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = (uint8_t)byte;
     }
   __syncthreads();
-  // coalesced 16-byte stores of the code tile
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = (tid >> 3) + 32 * j, c = tid & 7;
     if (r < rows)
       *reinterpret_cast<uint4*>(g.h + (long long)(row_begin + r) * g.I + n0 + c * 16) =
-          *reinterpret_cast<const uint4*>(lds_h + r * 128 + c * 16);
+          *reinterpret_cast<const uint4*>(stage_h + r * 128 + c * 16);
   }
 }
 
@@ -352,15 +391,11 @@ size_t gemm_max_mtiles(int rows_cap, int EL, int variant) {
   return ((size_t)rows_cap + (size_t)EL * (bm - 1)) / bm;
 }
 
-static hipError_t launch_gemm(const GemmArgs& a, int mode, int wfmt, size_t max_mt, hipStream_t s) {
-  const size_t grid = max_mt * (size_t)a.n_tiles;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  dim3 gr((unsigned)grid), bl(256);
-  if (mode == 1 && wfmt == 0) grouped_gemm_kernel<1, 0><<<gr, bl, 0, s>>>(a);
-  else if (mode == 1) grouped_gemm_kernel<1, 1><<<gr, bl, 0, s>>>(a);
-  else if (wfmt == 0) grouped_gemm_kernel<2, 0><<<gr, bl, 0, s>>>(a);
-  else grouped_gemm_kernel<2, 1><<<gr, bl, 0, s>>>(a);
+bool gemm_supports(int H, int I) { return H / kBK <= kMaxKSteps && I / kBK <= kMaxKSteps; }
+
+template <int MODE, int WFMT, int BN>
+static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
+  grouped_gemm_kernel<MODE, WFMT, BN><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -377,7 +412,10 @@ hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint
   a.b_estride = sh.wfmt == 0 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
   a.bsf_estride = sh.wfmt == 0 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
   a.act = sh.act; a.clamp = sh.clamp; a.alpha = sh.alpha; a.bias = sh.bias;
-  return launch_gemm(a, 1, sh.wfmt, gemm_max_mtiles(sh.T * sh.k, sh.EL, variant), s);
+  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  return sh.wfmt == 0 ? launch_one<1, 0, 256>(a, grid, s) : launch_one<1, 1, 256>(a, grid, s);
 }
 
 hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
@@ -387,10 +425,15 @@ hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint
   if (err != hipSuccess) return err;
   GemmArgs a{};
   a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets; a.plan = plan; a.y2 = y2;
-  a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.n_tiles = (sh.H + kBN - 1) / kBN;
+  a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL;
   a.b_estride = sh.wfmt == 0 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt == 0 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
-  return launch_gemm(a, 2, sh.wfmt, gemm_max_mtiles(sh.T * sh.k, sh.EL, variant), s);
+  const int bn = 256;
+  a.n_tiles = (sh.H + bn - 1) / bn;
+  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  return sh.wfmt == 0 ? launch_one<2, 0, 256>(a, grid, s) : launch_one<2, 1, 256>(a, grid, s);
 }
 
 }  // namespace moe

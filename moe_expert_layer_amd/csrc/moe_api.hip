@@ -105,6 +105,8 @@ moe_status check_desc(const moe_layer_desc* d) {
       return fail(MOE_ERR_INVALID_DESC, "act_alpha / act_up_bias must be finite");
   }
   if (d->variant < -1 || d->variant > 1) return fail(MOE_ERR_INVALID_DESC, "variant %d unknown", d->variant);
+  if (!moe::gemm_supports(d->hidden, d->inter))
+    return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d above the supported 8192", d->hidden, d->inter);
   return MOE_OK;
 }
 

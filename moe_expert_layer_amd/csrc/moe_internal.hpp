@@ -27,6 +27,8 @@ hipError_t launch_permute(const int32_t* ids, int nslots, int e0, int EL, int32_
 // grouped GEMMs ------------------------------------------------------------
 // Tile plan: plan[e] = first m-tile of local expert e, plan[EL] = number of m-tiles.
 int gemm_block_m(int variant);
+// largest contraction the GEMM kernels stage scales for (K / 128 <= 64)
+bool gemm_supports(int H, int I);
 size_t gemm_max_mtiles(int rows_cap, int EL, int variant);
 hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
                       const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
