@@ -55,7 +55,8 @@
  *     HIP graph.  Calls on distinct workspaces may run concurrently.
  *   - Alignment: x, x_sf, w1, w2, h, logits, y and the workspace must be 16-byte
  *     aligned (the workspace 256-byte aligned).
- *   - Limits: H and I multiples of 128; 1 <= E_loc <= E_tot <= 1024;
+ *   - Limits: H and I multiples of 128 and at most 8192 (MOE_ERR_UNSUPPORTED above);
+ *     1 <= E_loc <= E_tot <= 1024;
  *     1 <= k <= min(E_tot, 16); T*k < 2^31.
  */
 #ifndef MOE_EXPERT_LAYER_H_
@@ -99,7 +100,7 @@ typedef struct {
   float act_clamp;        /* OAI only: gate <= clamp, |up| <= clamp; +inf = no clamp (must be > 0) */
   float act_alpha;        /* OAI only: sigmoid(alpha * gate); default 1.0 */
   float act_up_bias;      /* OAI only: (up + up_bias); default 0.0 */
-  int32_t variant;        /* -1 = heuristic kernel choice; 0 = general tiles; 1 = small-row tiles */
+  int32_t variant;        /* GEMM tiles: -1 = heuristic; 0 = 128-row tiles; 1 = 256-row tiles */
 } moe_layer_desc;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION at build time). */

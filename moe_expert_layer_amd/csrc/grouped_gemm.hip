@@ -30,10 +30,11 @@
 // consumed, and the loads take no registers.  The waits are explicit (s_waitcnt vmcnt +
 // s_barrier).  LDS rows are 16-byte-chunk XOR swizzled so the operand reads are bank
 // conflict free.  Workgroups map to tiles in an XCD-aware order (consecutive tiles of one
-// expert on one XCD, sharing its L2).  Row tiles past an expert's last row skip their
-// MFMAs (decode-sized experts).
+// expert on one XCD, sharing its L2).  Waves whose rows all lie past an expert's last row
+// skip their MFMAs (decode-sized experts).
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "moe_internal.hpp"
@@ -42,10 +43,8 @@ namespace moe {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;       // rows per tile
-constexpr int kBK = 128;       // K per stage
 constexpr int kGroupN = 8;     // n-tiles per group in the tile order
-constexpr int kMaxKSteps = 64; // K <= 8192 (scales of a tile are staged in LDS)
+constexpr int kMaxKSteps = 64; // K <= 8192 (scales of a tile are staged in LDS, one per 128-wide step)
 
 struct GemmArgs {
   const uint8_t* A;      // FC1: x [T, K]; FC2: h [cap, K]
@@ -70,21 +69,40 @@ struct GemmArgs {
   float clamp, alpha, bias;
 };
 
-template <int MODE, int WFMT, int BN>
+// Tile shape: BM rows x BN weight rows, K advancing BK per stage through an NSTAGE ring,
+// NW waves arranged (BM/WTM) x 2, each wave WTM rows x BN/2 weight rows.  PIPE: the operand
+// fragments of stage ks+1 are read from LDS while the MFMAs of stage ks run.
+template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
 struct Cfg {
-  static constexpr int NSTAGE = (WFMT == 0 && BN == 256) ? 3 : 4;
-  static constexpr int B_ROWB = WFMT == 0 ? 128 : 64;      // weight bytes per row per stage
-  static constexpr int A_BYTES = kBM * 128;                // 16 KB
+  static constexpr int NTHR = NW * 64;
+  static constexpr int WM = BM / WTM;                       // waves along M
+  static constexpr int MI = WTM / 32;                       // 32-row tiles per wave
+  static constexpr int A_ROWB = BK;                         // bytes per activation row per stage
+  static constexpr int B_ROWB = WFMT == 0 ? BK : BK / 2;    // bytes per weight row per stage
+  static constexpr int A_BYTES = BM * A_ROWB;
   static constexpr int B_BYTES = BN * B_ROWB;
-  static constexpr int S_BYTES = WFMT == 1 ? BN * 4 : 0;   // MXFP4 scale dwords per stage
+  static constexpr int S_BYTES = WFMT == 1 ? NW * 256 : 0;  // MXFP4 scale dwords (64 rows per wave)
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int A_DMA = A_BYTES / 1024 / 4;         // 16-byte DMA instructions per wave per stage
-  static constexpr int B_DMA = B_BYTES / 1024 / 4;
-  static constexpr int S_DMA = WFMT == 1 ? S_BYTES / 256 / 4 : 0;  // 4-byte DMA instructions per wave
+  static constexpr int A_DMA = A_BYTES / 1024 / NW;         // 16-byte DMA instructions per wave per stage
+  static constexpr int B_DMA = B_BYTES / 1024 / NW;
+  static constexpr int S_DMA = WFMT == 1 ? 1 : 0;           // 4-byte DMA instructions per wave per stage
   static constexpr int PER_STAGE = A_DMA + B_DMA + S_DMA;
-  static constexpr int NT = BN / 2 / 32;                   // 32-wide column tiles per wave
-  static constexpr int A_ROWS_PER_KB = 1024 / 128;         // rows per 1 KB DMA block
-  static constexpr int B_ROWS_PER_KB = 1024 / B_ROWB;
+  static constexpr int NT = BN / 2 / 32;                    // 32-wide column tiles per wave
+  static constexpr int NH = BK / 64;                        // 64-wide MFMA K steps per stage
+  static constexpr int A_CPR = A_ROWB / 16, B_CPR = B_ROWB / 16;  // 16-byte chunks per row
+  static_assert(WM * 2 == NW, "waves must cover the tile");
+  static_assert(A_DMA >= 1 && B_DMA >= 1 && A_DMA * NW * 1024 == A_BYTES && B_DMA * NW * 1024 == B_BYTES, "");
+  static_assert(WFMT == 0 || BN <= NW * 64, "one scale DMA per wave covers 64 weight rows");
+  static_assert(!PIPE || NSTAGE >= 3, "pipelined fragments need the next stage resident");
+};
+
+// Operand fragments of one stage for one wave (A rows, B columns, their scale bytes).
+template <int MI, int NT, int NH>
+struct Frags {
+  v8i a[NH][MI];
+  v8i b[NH][NT];
+  int sa[MI];
+  int sb[NH][NT];
 };
 
 // ---------------------------------------------------------------------------------------
@@ -103,9 +121,14 @@ __device__ __forceinline__ void wait_vm_barrier() {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// XOR swizzles of 16-byte chunks: conflict-free for 8 (and 16) consecutive rows read at one chunk
-__device__ __forceinline__ int g8(int r) { return (r ^ (r >> 3)) & 7; }         // 128-byte rows
-__device__ __forceinline__ int g4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }  // 64-byte rows
+// XOR swizzles of 16-byte chunks, conflict-free when 8 (or 16) consecutive rows are read at
+// one logical chunk: rows of 128, 64 and 32 bytes.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if (CPR == 8) return (r ^ (r >> 3)) & 7;
+  if (CPR == 4) return ((r >> 1) ^ (r >> 3)) & 3;
+  return ((r >> 2) ^ (r >> 3)) & 1;
+}
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -118,14 +141,15 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ plan, int
   return lo;
 }
 
-template <int MODE, int WFMT, int BN>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
-  using C = Cfg<MODE, WFMT, BN>;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NSTAGE * C::STAGE];
-  __shared__ uint8_t s_asf[kMaxKSteps * kBM];  // [ks][row] activation scales
-  __shared__ uint8_t s_bsf[2 * kMaxKSteps];    // [block][ks] FP8 weight scales
-  __shared__ int s_tok[kBM];
-  __shared__ float s_amax[2][kBM];
+template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
+__global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(GemmArgs g) {
+  using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
+  using F = Frags<C::MI, C::NT, C::NH>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTAGE * C::STAGE];
+  __shared__ uint8_t s_asf[kMaxKSteps * BM];  // [ks128][row] activation scales
+  __shared__ uint8_t s_bsf[2 * kMaxKSteps];   // [block][ks128] FP8 weight scales
+  __shared__ int s_tok[BM];
+  __shared__ float s_amax[2][BM];
 
   const int total = g.plan[g.EL] * g.n_tiles;
   const int bid = blockIdx.x;
@@ -144,33 +168,34 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
   const int idx = li - grp * gn * mt_e;
   const int m_tile = idx / gsz;
   const int n_tile = grp * gn + idx % gsz;
-  const int row_begin = g.offsets[e] + m_tile * kBM;
-  const int rows = min(kBM, g.offsets[e + 1] - row_begin);
+  const int row_begin = g.offsets[e] + m_tile * BM;
+  const int rows = min(BM, g.offsets[e + 1] - row_begin);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int nk = g.K / kBK;
+  const int wm = wave % C::WM, wn = wave / C::WM;
+  const int nk = g.K / BK;       // stages
+  const int nk128 = g.K / 128;   // scale steps
   const int n0 = MODE == 1 ? n_tile * 128 : n_tile * BN;
 
   // ---- A row sources (token rows for FC1) and scales staged in LDS ----
-  if (tid < kBM) {
-    const int r = tid < rows ? tid : 0;
-    s_tok[tid] = MODE == 1 ? g.row_to_slot[row_begin + r] / g.k : row_begin + r;
+  for (int i = tid; i < BM; i += C::NTHR) {
+    const int r = i < rows ? i : 0;
+    s_tok[i] = MODE == 1 ? g.row_to_slot[row_begin + r] / g.k : row_begin + r;
   }
   __syncthreads();
-  for (int i = tid; i < nk * kBM; i += 256) {
-    const int ks = i / kBM, r = i - ks * kBM;
-    s_asf[i] = g.A_sf[(long long)s_tok[r] * nk + ks];
+  for (int i = tid; i < nk128 * BM; i += C::NTHR) {
+    const int ks = i / BM, r = i - ks * BM;
+    s_asf[i] = g.A_sf[(long long)s_tok[r] * nk128 + ks];
   }
   const uint8_t* bsf_e = g.B_sf + (long long)e * g.bsf_estride;
   if (WFMT == 0) {
     // block rows: FC1 gate n0/128 and up (I+n0)/128; FC2 n0/128 and n0/128 + 1 (clamped)
-    for (int i = tid; i < 2 * nk; i += 256) {
-      const int blk = i / nk, ks = i - blk * nk;
+    for (int i = tid; i < 2 * nk128; i += C::NTHR) {
+      const int blk = i / nk128, ks = i - blk * nk128;
       int br;
       if (MODE == 1) br = blk == 0 ? n0 / 128 : (g.I + n0) / 128;
       else br = min(n0 / 128 + blk, g.N / 128 - 1);
-      s_bsf[i] = bsf_e[(long long)br * nk + ks];
+      s_bsf[i] = bsf_e[(long long)br * nk128 + ks];
     }
   }
 
@@ -178,8 +203,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
   const uint8_t* a_src[C::A_DMA];
 #pragma unroll
   for (int j = 0; j < C::A_DMA; ++j) {
-    const int r = (wave * C::A_DMA + j) * C::A_ROWS_PER_KB + (lane >> 3);
-    const int c = (lane & 7) ^ g8(r);
+    const int r = (wave * C::A_DMA + j) * (64 / C::A_CPR) + lane / C::A_CPR;
+    const int c = (lane % C::A_CPR) ^ swz<C::A_CPR>(r);
     a_src[j] = g.A + (long long)s_tok[r] * g.K + c * 16;
   }
   const uint8_t* b_e = g.B + (long long)e * g.b_estride;
@@ -188,127 +213,168 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
     const int rr = n0 + n;
     return rr < g.N ? rr : g.N - 1;
   };
+  const long long b_ld = WFMT == 0 ? g.K : g.K / 2;
   const uint8_t* b_src[C::B_DMA];
 #pragma unroll
   for (int j = 0; j < C::B_DMA; ++j) {
-    if (WFMT == 0) {
-      const int n = (wave * C::B_DMA + j) * C::B_ROWS_PER_KB + (lane >> 3);
-      const int c = (lane & 7) ^ g8(n);
-      b_src[j] = b_e + (long long)b_row(n) * g.K + c * 16;
-    } else {
-      const int n = (wave * C::B_DMA + j) * C::B_ROWS_PER_KB + (lane >> 2);
-      const int c = (lane & 3) ^ g4(n);
-      b_src[j] = b_e + (long long)b_row(n) * (g.K / 2) + c * 16;
-    }
+    const int n = (wave * C::B_DMA + j) * (64 / C::B_CPR) + lane / C::B_CPR;
+    const int c = (lane % C::B_CPR) ^ swz<C::B_CPR>(n);
+    b_src[j] = b_e + (long long)b_row(n) * b_ld + c * 16;
   }
-  const uint8_t* s_src = nullptr;  // MXFP4: lane owns weight row wave*64 + lane (4 scale bytes per stage)
-  if (WFMT == 1) s_src = bsf_e + (long long)b_row(wave * 64 + lane) * (g.K / 32);
+  // MXFP4: wave w loads the scale dword (4 blocks of 32 = one 128-wide K step) of weight rows
+  // (w % (BN/64)) * 64 + lane; waves beyond BN/64 load a second copy that is never read
+  const uint8_t* s_src = nullptr;
+  if (WFMT == 1) s_src = bsf_e + (long long)b_row((wave % (BN / 64)) * 64 + lane) * (g.K / 32);
 
   const uint32_t ring0 = lds_addr(ring);
   auto issue = [&](int ks) {
-    const uint32_t st = ring0 + (uint32_t)((ks % C::NSTAGE) * C::STAGE);
+    const uint32_t st = ring0 + (uint32_t)((ks % NSTAGE) * C::STAGE);
 #pragma unroll
     for (int j = 0; j < C::A_DMA; ++j)
-      dma16(a_src[j] + ks * kBK, uniform(st + (wave * C::A_DMA + j) * 1024));
+      dma16(a_src[j] + (long long)ks * C::A_ROWB, uniform(st + (wave * C::A_DMA + j) * 1024));
 #pragma unroll
     for (int j = 0; j < C::B_DMA; ++j)
-      dma16(b_src[j] + ks * (WFMT == 0 ? kBK : kBK / 2), uniform(st + C::A_BYTES + (wave * C::B_DMA + j) * 1024));
-    if (WFMT == 1) dma4(s_src + ks * 4, uniform(st + C::A_BYTES + C::B_BYTES + wave * 256));
+      dma16(b_src[j] + (long long)ks * C::B_ROWB, uniform(st + C::A_BYTES + (wave * C::B_DMA + j) * 1024));
+    if (WFMT == 1)
+      dma4(s_src + ((ks * BK) / 128) * 4, uniform(st + C::A_BYTES + C::B_BYTES + wave * 256));
+  };
+  // wait until at most `ahead` stages of this wave's DMA are in flight, then workgroup barrier
+  auto wait_stages = [&](int ahead) {
+    if (ahead >= 2) wait_vm_barrier<2 * C::PER_STAGE>();
+    else if (ahead == 1) wait_vm_barrier<C::PER_STAGE>();
+    else wait_vm_barrier<0>();
   };
 
-  v16f acc[2][C::NT];
+  v16f acc[C::MI][C::NT];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int ct = 0; ct < C::NT; ++ct)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mi][ct][i] = 0.f;
 
   const int lrow = lane & 31, kb = lane >> 5;
-  bool mi_live[2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) mi_live[mi] = wm * 64 + mi * 32 < rows;
+  // a wave whose rows all lie past the expert's last row skips its MFMAs (decode-sized experts);
+  // the test is wave-uniform so the MFMA burst stays one straight-line block
+  const bool wave_live = wm * WTM < rows;
   // first weight row (tile-local) of column tile ct of this wave
   auto bcol = [&](int ct) -> int {
     if (MODE == 1) return ct < C::NT / 2 ? wn * 64 + ct * 32 : 128 + wn * 64 + (ct - C::NT / 2) * 32;
     return wn * (BN / 2) + ct * 32;
   };
 
-  // prologue: NSTAGE-1 stages in flight
-#pragma unroll
-  for (int s = 0; s < C::NSTAGE - 1; ++s)
-    if (s < nk) issue(s);
-
-  for (int ks = 0; ks < nk; ++ks) {
-    const int rem = nk - 1 - ks;
-    if (C::NSTAGE == 4 && rem >= 2) wait_vm_barrier<2 * C::PER_STAGE>();
-    else if (rem >= 1) wait_vm_barrier<C::PER_STAGE>();
-    else wait_vm_barrier<0>();
-    if (ks + C::NSTAGE - 1 < nk) issue(ks + C::NSTAGE - 1);
-
-    const uint8_t* st = ring + (ks % C::NSTAGE) * C::STAGE;
+  // operand fragments of stage ks from its ring slot
+  auto load = [&](int ks, F& f) {
+    const uint8_t* st = ring + (ks % NSTAGE) * C::STAGE;
     const uint8_t* sa_ = st;
     const uint8_t* sb_ = st + C::A_BYTES;
-    int sa[2];
+    const int k128 = (ks * BK) / 128;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) sa[mi] = s_asf[ks * kBM + wm * 64 + mi * 32 + lrow];
+    for (int mi = 0; mi < C::MI; ++mi) f.sa[mi] = s_asf[k128 * BM + wm * WTM + mi * 32 + lrow];
     int sbu0 = 0, sbu1 = 0;
     if (WFMT == 0) {
-      if (MODE == 1) { sbu0 = s_bsf[ks]; sbu1 = s_bsf[nk + ks]; }
-      else { sbu0 = s_bsf[(BN == 256 ? wn : 0) * nk + ks]; sbu1 = sbu0; }
+      if (MODE == 1) { sbu0 = s_bsf[k128]; sbu1 = s_bsf[nk128 + k128]; }
+      else { sbu0 = s_bsf[(BN == 256 ? wn : 0) * nk128 + k128]; sbu1 = sbu0; }
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v8i af[2];
+    for (int h = 0; h < C::NH; ++h) {
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int r = wm * 64 + mi * 32 + lrow;
-        const uint4 lo = lds16(sa_ + r * 128 + (((4 * h + kb) ^ g8(r)) << 4));
-        const uint4 hi = lds16(sa_ + r * 128 + (((4 * h + 2 + kb) ^ g8(r)) << 4));
-        af[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      for (int mi = 0; mi < C::MI; ++mi) {
+        const int r = wm * WTM + mi * 32 + lrow;
+        const uint4 lo = lds16(sa_ + r * C::A_ROWB + (((4 * h + kb) ^ swz<C::A_CPR>(r)) << 4));
+        const uint4 hi = lds16(sa_ + r * C::A_ROWB + (((4 * h + 2 + kb) ^ swz<C::A_CPR>(r)) << 4));
+        f.a[h][mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
       for (int ct = 0; ct < C::NT; ++ct) {
         const int n = bcol(ct) + lrow;
-        v8i bf;
-        int sb;
         if (WFMT == 0) {
-          const uint4 lo = lds16(sb_ + n * 128 + (((4 * h + kb) ^ g8(n)) << 4));
-          const uint4 hi = lds16(sb_ + n * 128 + (((4 * h + 2 + kb) ^ g8(n)) << 4));
-          bf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sb = (MODE == 1 && ct >= C::NT / 2) ? sbu1 : sbu0;
+          const uint4 lo = lds16(sb_ + n * C::B_ROWB + (((4 * h + kb) ^ swz<C::B_CPR>(n)) << 4));
+          const uint4 hi = lds16(sb_ + n * C::B_ROWB + (((4 * h + 2 + kb) ^ swz<C::B_CPR>(n)) << 4));
+          f.b[h][ct] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          f.sb[h][ct] = (MODE == 1 && ct >= C::NT / 2) ? sbu1 : sbu0;
         } else {
-          const uint4 q = lds16(sb_ + n * 64 + (((2 * h + kb) ^ g4(n)) << 4));
-          bf = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          const uint4 q = lds16(sb_ + n * C::B_ROWB + (((2 * h + kb) ^ swz<C::B_CPR>(n)) << 4));
+          f.b[h][ct] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
           const int dw = *reinterpret_cast<const int*>(st + C::A_BYTES + C::B_BYTES + n * 4);
-          sb = (dw >> (8 * (2 * h + kb))) & 0xff;
+          const int blk = ((ks * BK) % 128) / 32 + 2 * h + kb;  // 32-wide block inside the 128-wide step
+          f.sb[h][ct] = (dw >> (8 * blk)) & 0xff;
         }
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          if (mi_live[mi])
-            acc[mi][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf, acc[mi][ct], 0,
-                                                                          WFMT == 0 ? 0 : 4, 0, sa[mi], 0, sb);
       }
+    }
+  };
+  // MFMAs of one stage for the first NL row tiles of the wave (row tiles past the expert's last
+  // row are skipped; NL is wave-uniform, so each case is one straight-line MFMA burst)
+  auto mma_n = [&](const F& f, auto nl) {
+    constexpr int NL = decltype(nl)::value;
+#pragma unroll
+    for (int h = 0; h < C::NH; ++h)
+#pragma unroll
+      for (int ct = 0; ct < C::NT; ++ct)
+#pragma unroll
+        for (int mi = 0; mi < NL; ++mi)
+          acc[mi][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[h][mi], f.b[h][ct], acc[mi][ct], 0,
+                                                                        WFMT == 0 ? 0 : 4, 0, f.sa[mi], 0,
+                                                                        f.sb[h][ct]);
+  };
+  const int live_tiles = min(C::MI, max(0, (rows - wm * WTM + 31) / 32));
+  auto mma = [&](const F& f) {
+    if (BM != 128 || live_tiles >= C::MI) mma_n(f, std::integral_constant<int, C::MI>{});  // 128-row tiles only
+    else if (C::MI > 1 && live_tiles == 1) mma_n(f, std::integral_constant<int, 1>{});
+    else if (C::MI > 2 && live_tiles == 2) mma_n(f, std::integral_constant<int, (C::MI > 2 ? 2 : 1)>{});
+    else if (C::MI > 3 && live_tiles == 3) mma_n(f, std::integral_constant<int, (C::MI > 3 ? 3 : 1)>{});
+  };
+
+  // prologue: NSTAGE-1 stages in flight
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < nk) issue(s);
+
+  if (!PIPE) {
+    for (int ks = 0; ks < nk; ++ks) {
+      wait_stages(min(nk - 1 - ks, NSTAGE - 2));
+      if (ks + NSTAGE - 1 < nk) issue(ks + NSTAGE - 1);
+      if (!wave_live) continue;
+      F f;
+      load(ks, f);
+      mma(f);
+    }
+  } else {
+    // stage ks+1 must be resident while stage ks multiplies: one stage less of DMA lookahead
+    F f0, f1;
+    wait_stages(min(nk - 1, NSTAGE - 2));
+    if (wave_live) load(0, f0);
+    auto step = [&](int ks, F& cur, F& nxt) {
+      if (ks + 1 < nk) {
+        wait_stages(min(nk - 2 - ks, NSTAGE - 3));
+        if (ks + NSTAGE - 1 < nk) issue(ks + NSTAGE - 1);
+        if (wave_live) load(ks + 1, nxt);
+      }
+      if (wave_live) mma(cur);
+    };
+    for (int ks = 0; ks < nk; ks += 2) {
+      step(ks, f0, f1);
+      if (ks + 1 < nk) step(ks + 1, f1, f0);
     }
   }
 
   if (MODE == 2) {
     // ---- FC2 epilogue: fp32 rows of Y2 (32 consecutive columns per lane group) ----
+    if (wave_live) {
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      if (!mi_live[mi]) continue;
+      for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
-        if (r < rows) {
-          float* dst = g.y2 + (long long)(row_begin + r) * g.N;
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
+          if (r < rows) {
+            float* dst = g.y2 + (long long)(row_begin + r) * g.N;
 #pragma unroll
-          for (int ct = 0; ct < C::NT; ++ct) {
-            const int col = n0 + bcol(ct) + lrow;
-            if (col < g.N) dst[col] = acc[mi][ct][i];
+            for (int ct = 0; ct < C::NT; ++ct) {
+              const int col = n0 + bcol(ct) + lrow;
+              if (col < g.N) dst[col] = acc[mi][ct][i];
+            }
           }
         }
-      }
     }
     return;
   }
@@ -317,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
   // lane holds rows 8*(i/4) + 4*kb + i%4 of each row tile; h column wn*64 + c*32 + lrow (c = 0, 1)
   constexpr int NC = C::NT / 2;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -334,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
         acc[mi][c][i] = hh;  // h overwrites the gate accumulator
       }
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float m = 0.f;
@@ -342,15 +408,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
       for (int c = 0; c < NC; ++c) m = fmaxf(m, fabsf(acc[mi][c][i]));
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-      if (lrow == 0) s_amax[wn][wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3)] = m;
+      if (lrow == 0) s_amax[wn][wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3)] = m;
     }
   __syncthreads();  // every wave is past its last ring read; s_amax complete
-  uint8_t* stage_h = ring;  // [128 rows][128 B] code tile
+  uint8_t* stage_h = ring;  // [BM rows][128 B] code tile
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
+      const int r = wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
       const float amax = fmaxf(s_amax[0][r], s_amax[1][r]);
       const int byte = ue8m0_for_amax(amax);
       const float inv = inv_scale_of(byte);
@@ -362,9 +428,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g) {
       if (wn == 0 && lrow == 0 && r < rows) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = (uint8_t)byte;
     }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (tid >> 3) + 32 * j, c = tid & 7;
+  for (int q = tid; q < BM * 8; q += C::NTHR) {
+    const int r = q >> 3, c = q & 7;
     if (r < rows)
       *reinterpret_cast<uint4*>(g.h + (long long)(row_begin + r) * g.I + n0 + c * 16) =
           *reinterpret_cast<const uint4*>(stage_h + r * 128 + c * 16);
@@ -383,7 +448,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e <= EL; e += 1024) plan[e] = a[e];
 }
 
-int gemm_block_m(int /*variant*/) { return kBM; }
+// variant 0: 128-row tiles (4 waves, 128-K stages x 3): experts with few rows (decode).
+// variant 1: 256-row tiles (8 waves of 64x128, 128-K stages x 2): experts with many rows
+//            (prefill).  Measured on the prefill share against 64-K x 4 stages, 128x128 wave
+//            tiles and fragments read one stage ahead: this shape was fastest.
+int gemm_block_m(int variant) { return variant == 1 ? 256 : 128; }
 
 size_t gemm_max_mtiles(int rows_cap, int EL, int variant) {
   const int bm = gemm_block_m(variant);
@@ -391,12 +460,22 @@ size_t gemm_max_mtiles(int rows_cap, int EL, int variant) {
   return ((size_t)rows_cap + (size_t)EL * (bm - 1)) / bm;
 }
 
-bool gemm_supports(int H, int I) { return H / kBK <= kMaxKSteps && I / kBK <= kMaxKSteps; }
+bool gemm_supports(int H, int I) { return H / 128 <= kMaxKSteps && I / 128 <= kMaxKSteps; }
 
-template <int MODE, int WFMT, int BN>
+template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
 static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
-  grouped_gemm_kernel<MODE, WFMT, BN><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE><<<dim3((unsigned)grid), dim3(NW * 64), 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_t grid, hipStream_t s) {
+  if (variant == 1) {
+    return wfmt == 0 ? launch_one<MODE, 0, 256, 256, 128, 2, 8, 64, 0>(a, grid, s)
+                     : launch_one<MODE, 1, 256, 256, 128, 2, 8, 64, 0>(a, grid, s);
+  }
+  return wfmt == 0 ? launch_one<MODE, 0, 128, 256, 128, 3, 4, 64, 0>(a, grid, s)
+                   : launch_one<MODE, 1, 128, 256, 128, 4, 4, 64, 0>(a, grid, s);
 }
 
 hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
@@ -415,7 +494,7 @@ hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint
   const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  return sh.wfmt == 0 ? launch_one<1, 0, 256>(a, grid, s) : launch_one<1, 1, 256>(a, grid, s);
+  return launch_variant<1>(a, sh.wfmt, variant, grid, s);
 }
 
 hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
@@ -428,12 +507,11 @@ hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint
   a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL;
   a.b_estride = sh.wfmt == 0 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt == 0 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
-  const int bn = 256;
-  a.n_tiles = (sh.H + bn - 1) / bn;
+  a.n_tiles = (sh.H + 255) / 256;
   const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  return sh.wfmt == 0 ? launch_one<2, 0, 256>(a, grid, s) : launch_one<2, 1, 256>(a, grid, s);
+  return launch_variant<2>(a, sh.wfmt, variant, grid, s);
 }
 
 }  // namespace moe

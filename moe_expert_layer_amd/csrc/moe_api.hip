@@ -153,7 +153,14 @@ moe::Shape shape_of(const moe_layer_desc& d) {
   return s;
 }
 
-int pick_variant(const moe_layer_desc& d) { return d.variant < 0 ? 0 : d.variant; }
+// Tile variant: 256-row tiles once an expert can hold 256 rows on average (T * min(k, E_loc)
+// rows spread over E_loc experts is the most the routing can give them), else 128-row tiles.
+// Chosen from the descriptor only, so no host synchronisation is needed.
+int pick_variant(const moe_layer_desc& d) {
+  if (d.variant >= 0) return d.variant;
+  const long long most_rows = (long long)d.num_tokens * (d.topk < d.num_local ? d.topk : d.num_local);
+  return most_rows >= 256LL * d.num_local ? 1 : 0;
+}
 
 #define MOE_TRY_HIP(call)                                                            \
   do {                                                                               \

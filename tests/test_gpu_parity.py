@@ -67,6 +67,21 @@ def test_layer_parity_small(name, w):
     assert np.all(fused["y_bf16"][nol] == 0)
 
 
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("name", ["ragged_oai", "zipf_small", "mxfp4_small", "k16_e1024"])
+def test_layer_parity_forced_variant(name, variant):
+    w = dict(_small_cases())[name]
+    G.say(f"[variant] {name} variant={variant}")
+    inp = synth.generate(w)
+    ref = O.layer(w, inp)
+    got = G.run_split(w, G.upload(inp), variant=variant)
+    G.check_routing(got, ref)
+    be, se = G.h_agreement(got["h"], got["h_sf"], ref["h"], ref["h_sf"])
+    err = G.rel_fro(G.bf16_to_f64(got["y_bf16"]), G.bf16_to_f64(ref["y_bf16"]))
+    G.say(f"[variant] {name} variant={variant}: rel_fro={err:.3e} h_bytes_equal={be:.5f}")
+    assert be >= 0.99 and se >= 0.99 and err <= TOL
+
+
 def test_run_twice_bit_identical():
     w = synth.shrink(synth.workload("oai"), tokens=300, hidden=768, inter=256, seed=20)
     inp = synth.generate(w)
