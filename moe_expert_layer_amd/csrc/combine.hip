@@ -5,8 +5,8 @@
 // get +0.  Sources: "Pull Style Cutedsl Megakernel" (Layout: the top-k reduce after
 // the fused FC1/FC2 schedule) and "Optimize sm100 version with token-aware BM240
 // tiling, native UE8M0, and direct combine" (description: combine into token order).
-// One workgroup per token; every output element is written by exactly one thread, so
-// the result does not depend on scheduling.
+// Every output element is written by exactly one thread, so the result does not depend
+// on scheduling.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -15,41 +15,69 @@
 
 namespace moe {
 
+// grid (ceil(H / 2048), min(T, 65535)): a workgroup owns 2048 columns of one token at a time
+// (tokens strided by the grid height); thread i handles columns 4i.. and 1024 + 4i.., so each
+// load instruction of the workgroup reads 4 KB of one Y2 row.  The token's slots are taken in
+// batches of four whose row loads are all issued before the in-order accumulation.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y2, const int32_t* __restrict__ s2r,
-                                                      const float* __restrict__ w, int H, int k,
+                                                      const float* __restrict__ w, int T, int H, int k,
                                                       uint16_t* __restrict__ y) {
-  __shared__ int rows[kMaxTopk];
-  __shared__ float wt[kMaxTopk];
-  const int t = blockIdx.x;
-  if (threadIdx.x < k) {
-    rows[threadIdx.x] = s2r[(long long)t * k + threadIdx.x];
-    wt[threadIdx.x] = w[(long long)t * k + threadIdx.x];
-  }
-  __syncthreads();
-  uint16_t* yt = y + (long long)t * H;
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      if (r >= 0) {
-        const float4 v = *reinterpret_cast<const float4*>(y2 + (long long)r * H + c);
-        const float ww = wt[j];
-        a0 = fmaf(ww, v.x, a0);
-        a1 = fmaf(ww, v.y, a1);
-        a2 = fmaf(ww, v.z, a2);
-        a3 = fmaf(ww, v.w, a3);
+  const int c0 = blockIdx.x * 2048 + threadIdx.x * 4;
+  if (c0 >= H) return;
+  const bool two = c0 + 1024 < H;
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      int rows[4];
+      float wt[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {  // slots in slot order; -1 = not local
+        const int j = j0 + jj;
+        rows[jj] = j < k ? s2r[(long long)t * k + j] : -1;
+        wt[jj] = rows[jj] >= 0 ? w[(long long)t * k + j] : 0.f;
+      }
+      float4 v0[4], v1[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if (rows[jj] >= 0) {
+          const float* src = y2 + (long long)rows[jj] * H + c0;
+          v0[jj] = *reinterpret_cast<const float4*>(src);
+          if (two) v1[jj] = *reinterpret_cast<const float4*>(src + 1024);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if (rows[jj] >= 0) {
+          acc[0] = fmaf(wt[jj], v0[jj].x, acc[0]);
+          acc[1] = fmaf(wt[jj], v0[jj].y, acc[1]);
+          acc[2] = fmaf(wt[jj], v0[jj].z, acc[2]);
+          acc[3] = fmaf(wt[jj], v0[jj].w, acc[3]);
+          if (two) {
+            acc[4] = fmaf(wt[jj], v1[jj].x, acc[4]);
+            acc[5] = fmaf(wt[jj], v1[jj].y, acc[5]);
+            acc[6] = fmaf(wt[jj], v1[jj].z, acc[6]);
+            acc[7] = fmaf(wt[jj], v1[jj].w, acc[7]);
+          }
+        }
       }
     }
-    const uint32_t lo = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16_rne(a2) | ((uint32_t)f32_to_bf16_rne(a3) << 16);
-    *reinterpret_cast<uint2*>(yt + c) = make_uint2(lo, hi);
+    uint16_t* dst = y + (long long)t * H + c0;
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2((uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16),
+                   (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16));
+    if (two)
+      *reinterpret_cast<uint2*>(dst + 1024) =
+          make_uint2((uint32_t)f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16),
+                     (uint32_t)f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16));
   }
 }
 
 hipError_t launch_combine(const float* y2, const int32_t* slot_to_row, const float* topk_w, int T, int H, int k,
                           uint16_t* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  combine_kernel<<<T, 256, 0, s>>>(y2, slot_to_row, topk_w, H, k, y);
+  combine_kernel<<<dim3((H + 2047) / 2048, T < 65535 ? T : 65535), 256, 0, s>>>(y2, slot_to_row, topk_w, T, H, k, y);
   return hipGetLastError();
 }
 

@@ -142,14 +142,19 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ plan, int
 }
 
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
-__global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   using F = Frags<C::MI, C::NT, C::NH>;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTAGE * C::STAGE];
-  __shared__ uint8_t s_asf[kMaxKSteps * BM];  // [ks128][row] activation scales
-  __shared__ uint8_t s_bsf[2 * kMaxKSteps];   // [block][ks128] FP8 weight scales
-  __shared__ int s_tok[BM];
-  __shared__ float s_amax[2][BM];
+  // LDS (dynamic, sized at launch): the stage ring, then the tile's activation scales
+  // [ks128][row] and FP8 weight scales [block][ks128].  The token list of the tile rows and
+  // the epilogue's amax scratch live inside the ring while it is not in use.
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  uint8_t* ring = lds;
+  uint8_t* s_asf = lds + NSTAGE * C::STAGE;
+  const int nk128_ = g.K / 128;
+  uint8_t* s_bsf = s_asf + BM * nk128_;
+  int* s_tok = reinterpret_cast<int*>(ring + NSTAGE * C::STAGE - BM * 4);  // prologue only
+  float(*s_amax)[BM] = reinterpret_cast<float(*)[BM]>(ring + BM * 128);      // epilogue only
 
   const int total = g.plan[g.EL] * g.n_tiles;
   const int bid = blockIdx.x;
@@ -225,6 +230,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_gemm_kernel(GemmArgs g) {
   // (w % (BN/64)) * 64 + lane; waves beyond BN/64 load a second copy that is never read
   const uint8_t* s_src = nullptr;
   if (WFMT == 1) s_src = bsf_e + (long long)b_row((wave % (BN / 64)) * 64 + lane) * (g.K / 32);
+  __syncthreads();  // s_tok (inside the ring) is consumed before the ring is filled
 
   const uint32_t ring0 = lds_addr(ring);
   auto issue = [&](int ks) {
@@ -448,7 +454,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e <= EL; e += 1024) plan[e] = a[e];
 }
 
-// variant 0: 128-row tiles (4 waves, 128-K stages x 3): experts with few rows (decode).
+// variant 0: 128-row tiles, 4 waves (FC1: 64-K stages x 3, FC2: 128 columns, 128-K stages
+//            x 2), small enough for two workgroups per CU: experts with few rows (decode).
 // variant 1: 256-row tiles (8 waves of 64x128, 128-K stages x 2): experts with many rows
 //            (prefill).  Measured on the prefill share against 64-K x 4 stages, 128x128 wave
 //            tiles and fragments read one stage ahead: this shape was fastest.
@@ -464,7 +471,14 @@ bool gemm_supports(int H, int I) { return H / 128 <= kMaxKSteps && I / 128 <= kM
 
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
 static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
-  grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE><<<dim3((unsigned)grid), dim3(NW * 64), 0, s>>>(a);
+  using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
+  static_assert(NSTAGE * C::STAGE >= BM * 128 + 2 * BM * 4 && NSTAGE * C::STAGE >= BM * 4 + BM * 128,
+                "the ring must hold the epilogue staging and the tile's token list");
+  auto kern = grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
+  const size_t lds = (size_t)NSTAGE * C::STAGE + (size_t)BM * (a.K / 128) + 2 * (a.K / 128);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  kern<<<dim3((unsigned)grid), dim3(NW * 64), lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -474,16 +488,23 @@ static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_
     return wfmt == 0 ? launch_one<MODE, 0, 256, 256, 128, 2, 8, 64, 0>(a, grid, s)
                      : launch_one<MODE, 1, 256, 256, 128, 2, 8, 64, 0>(a, grid, s);
   }
-  return wfmt == 0 ? launch_one<MODE, 0, 128, 256, 128, 3, 4, 64, 0>(a, grid, s)
-                   : launch_one<MODE, 1, 128, 256, 128, 4, 4, 64, 0>(a, grid, s);
+  // small experts: two workgroups fit one CU (<= 80 KB of LDS each) so one streams weights
+  // while the other is in its prologue or epilogue; FC2 tiles are 128 columns wide
+  if (MODE == 2)
+    return wfmt == 0 ? launch_one<MODE, 0, 128, 128, 128, 2, 4, 64, 0>(a, grid, s)
+                     : launch_one<MODE, 1, 128, 128, 128, 2, 4, 64, 0>(a, grid, s);
+  return wfmt == 0 ? launch_one<MODE, 0, 128, 256, 64, 3, 4, 64, 0>(a, grid, s)
+                   : launch_one<MODE, 1, 128, 256, 64, 4, 4, 64, 0>(a, grid, s);
 }
 
 hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
                       const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
-                      uint8_t* h_sf, int32_t* plan, hipStream_t s) {
-  plan_kernel<<<1, 1024, 0, s>>>(offsets, sh.EL, gemm_block_m(variant), plan);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+                      uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s) {
+  if (!plan_ready) {
+    plan_kernel<<<1, 1024, 0, s>>>(offsets, sh.EL, gemm_block_m(variant), plan);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   GemmArgs a{};
   a.A = x; a.A_sf = x_sf; a.row_to_slot = row_to_slot; a.B = w1; a.B_sf = w1_sf;
   a.offsets = offsets; a.plan = plan; a.h = h; a.h_sf = h_sf;
@@ -498,16 +519,20 @@ hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint
 }
 
 hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
-                      const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, hipStream_t s) {
-  plan_kernel<<<1, 1024, 0, s>>>(offsets, sh.EL, gemm_block_m(variant), plan);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+                      const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, bool plan_ready,
+                      hipStream_t s) {
+  if (!plan_ready) {
+    plan_kernel<<<1, 1024, 0, s>>>(offsets, sh.EL, gemm_block_m(variant), plan);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   GemmArgs a{};
   a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets; a.plan = plan; a.y2 = y2;
   a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL;
   a.b_estride = sh.wfmt == 0 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt == 0 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
-  a.n_tiles = (sh.H + 255) / 256;
+  const int bn = variant == 1 ? 256 : 128;
+  a.n_tiles = (sh.H + bn - 1) / bn;
   const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;

@@ -177,7 +177,8 @@ moe_status run_route_permute(const moe_layer_desc& d, const Layout& L, const flo
   MOE_TRY_HIP(moe::launch_route_topk(logits, d.num_tokens, d.num_experts, d.topk, ids, w, s));
   MOE_TRY_HIP(moe::launch_permute(ids, d.num_tokens * d.topk, d.local_begin, d.num_local,
                                   region<int32_t>(ws, L.chunk_cnt), region<int32_t>(ws, L.chunk_base), counts,
-                                  offsets, r2s, s2r, s));
+                                  offsets, r2s, s2r, moe::gemm_block_m(pick_variant(d)),
+                                  region<int32_t>(ws, L.plan1), s));
   return MOE_OK;
 }
 
@@ -250,7 +251,7 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* d, const uint8_t* x, con
   const Layout L = make_layout(*d);
   const moe::Shape sh = shape_of(*d);
   MOE_TRY_HIP(moe::launch_fc1(sh, pick_variant(*d), x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
-                              region<int32_t>(ws, L.plan1), (hipStream_t)stream));
+                              region<int32_t>(ws, L.plan1), false, (hipStream_t)stream));
   return ok();
 }
 
@@ -270,7 +271,7 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* d, const uint8_t* h, co
   const moe::Shape sh = shape_of(*d);
   float* y2 = region<float>(ws, L.y2);
   MOE_TRY_HIP(moe::launch_fc2(sh, pick_variant(*d), h, h_sf, w2, w2_sf, offsets, y2, region<int32_t>(ws, L.plan2),
-                              (hipStream_t)stream));
+                              false, (hipStream_t)stream));
   MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, y, (hipStream_t)stream));
   return ok();
 }
@@ -301,8 +302,10 @@ moe_status moe_layer(const moe_layer_desc* d, const float* logits, const uint8_t
   float* y2 = region<float>(ws, L.y2);
   const int variant = pick_variant(*d);
   if (moe_status st = run_route_permute(*d, L, logits, ids, w, counts, offsets, r2s, s2r, ws, s)) return st;
-  MOE_TRY_HIP(moe::launch_fc1(sh, variant, x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf, region<int32_t>(ws, L.plan1), s));
-  MOE_TRY_HIP(moe::launch_fc2(sh, variant, h, h_sf, w2, w2_sf, offsets, y2, region<int32_t>(ws, L.plan2), s));
+  // the permute wrote the tile plan of these offsets (plan1) for this variant's tile rows
+  MOE_TRY_HIP(moe::launch_fc1(sh, variant, x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf, region<int32_t>(ws, L.plan1),
+                              true, s));
+  MOE_TRY_HIP(moe::launch_fc2(sh, variant, h, h_sf, w2, w2_sf, offsets, y2, region<int32_t>(ws, L.plan1), true, s));
   MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, y, s));
   return ok();
 }

@@ -9,6 +9,8 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 16;
 constexpr int kPermChunk = 4096;  // slots per permute workgroup
+constexpr int kPermSmallSlots = 16384;  // at most this many slots: one-workgroup permute
+constexpr int kPermSmallBuckets = 257;  // ... and at most 256 local experts
 
 struct Shape {
   int T, H, I, E, e0, EL, k;
@@ -19,10 +21,11 @@ struct Shape {
 
 // route + permute ----------------------------------------------------------
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
-// buckets: EL local experts + 1 trailing bucket for non-local slots
+// buckets: EL local experts + 1 trailing bucket for non-local slots.  Also writes the GEMM
+// tile plan for tiles of `bm` rows (plan[e] = first m-tile of expert e, plan[EL] = all).
 hipError_t launch_permute(const int32_t* ids, int nslots, int e0, int EL, int32_t* chunk_cnt, int32_t* chunk_base,
-                          int32_t* counts, int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row,
-                          hipStream_t s);
+                          int32_t* counts, int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row, int bm,
+                          int32_t* plan, hipStream_t s);
 
 // grouped GEMMs ------------------------------------------------------------
 // Tile plan: plan[e] = first m-tile of local expert e, plan[EL] = number of m-tiles.
@@ -30,11 +33,14 @@ int gemm_block_m(int variant);
 // largest contraction the GEMM kernels stage scales for (K / 128 <= 64)
 bool gemm_supports(int H, int I);
 size_t gemm_max_mtiles(int rows_cap, int EL, int variant);
+// plan_ready: `plan` already holds the tile plan of these offsets for this variant's tile rows
+// (written by launch_permute); otherwise it is computed first.
 hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
                       const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
-                      uint8_t* h_sf, int32_t* plan, hipStream_t s);
+                      uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s);
 hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
-                      const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, hipStream_t s);
+                      const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, bool plan_ready,
+                      hipStream_t s);
 
 // combine --------------------------------------------------------------------
 hipError_t launch_combine(const float* y2, const int32_t* slot_to_row, const float* topk_w, int T, int H, int k,

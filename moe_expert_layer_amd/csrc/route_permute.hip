@@ -19,7 +19,48 @@
 
 namespace moe {
 
-// One wave per token; lane l holds logits l, l+64, l+128, ... (VPL of them).
+// Selection keys: the logit's bits mapped so that unsigned order is float order (-0 is
+// folded onto +0 first, so equal logits compare equal), above the complemented expert id,
+// so the unsigned maximum is the largest logit and, among equal logits, the lowest id.
+// 0 is below every finite logit's key and marks a taken (or absent) expert.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~e;
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
+
+template <int CTRL>  // the 64-bit value of the lane the DPP pattern names
+__device__ __forceinline__ uint64_t dpp64(uint64_t x) {
+  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+  const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xf, 0xf, false);
+  const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xf, 0xf, false);
+  return ((uint64_t)h2 << 32) | l2;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+// maximum over the wave: quad xor-1 and xor-2 swaps and row rotations by 4 and 8 reduce each
+// 16-lane row, then the four row results are read into scalars (the result is uniform)
+__device__ __forceinline__ uint64_t wave_max64(uint64_t x) {
+  x = umax64(x, dpp64<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = umax64(x, dpp64<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = umax64(x, dpp64<0x124>(x));  // row_ror 4
+  x = umax64(x, dpp64<0x128>(x));  // row_ror 8
+  return umax64(umax64(readlane64(x, 0), readlane64(x, 16)), umax64(readlane64(x, 32), readlane64(x, 48)));
+}
+
+// One wave per token; lane l holds the keys of experts l, l+64, l+128, ... (VPL of them).
+// Round j takes the wave maximum of the untaken keys; lane j keeps slot j, so the softmax
+// needs one exp and one divide per lane, and its sum runs over the slots in order.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int32_t* __restrict__ ids, float* __restrict__ w) {
@@ -27,63 +68,37 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
   const float* row = logits + (size_t)t * E;
-  float v[VPL];
-  unsigned taken = 0;
+  uint64_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -INFINITY;
-    if (e >= E) taken |= 1u << i;
+    key[i] = e < E ? route_key(row[e], e) : 0ull;
   }
-  float sel_v[kMaxTopk];
-  int sel_i[kMaxTopk];
+  uint64_t mine = 0;  // lane j: the key of slot j
+  for (int j = 0; j < k; ++j) {
+    uint64_t b = key[0];
 #pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j) {
-    sel_v[j] = 0.f;
-    sel_i[j] = 0;
-    if (j < k) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
+    for (int i = 1; i < VPL; ++i) b = umax64(b, key[i]);
+    const uint64_t best = wave_max64(b);
+    const int id = key_id(best);
 #pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const bool free_ = !((taken >> i) & 1u);
-        if (free_ && (bi == INT_MAX || v[i] > bv)) {
-          bv = v[i];
-          bi = lane + 64 * i;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      sel_v[j] = bv;
-      sel_i[j] = bi;
-    }
+    for (int i = 0; i < VPL; ++i)
+      if (id == lane + 64 * i) key[i] = 0ull;
+    if (lane == j) mine = best;
   }
-  // softmax over the chosen logits in fp64: e_j = exp(l_j - l_0), S summed in slot order
-  double ex[kMaxTopk];
+  // softmax over the chosen logits in fp64: e_j = exp(l_j - l_0), S = e_0 + e_1 + ... in
+  // slot order, w_j = fp32(e_j / S)
+  const double l0 = (double)key_value(readlane64(mine, 0));
+  const double ex = lane < k ? exp((double)key_value(mine) - l0) : 0.0;
+  const int2 ex2 = *reinterpret_cast<const int2*>(&ex);
   double S = 0.0;
-  const double l0 = (double)sel_v[0];
-#pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j) {
-    ex[j] = 0.0;
-    if (j < k) {
-      ex[j] = exp((double)sel_v[j] - l0);
-      S = (j == 0) ? ex[0] : S + ex[j];
-    }
+  for (int j = 0; j < k; ++j) {
+    const int2 v = make_int2(__builtin_amdgcn_readlane(ex2.x, j), __builtin_amdgcn_readlane(ex2.y, j));
+    S = j == 0 ? *reinterpret_cast<const double*>(&v) : S + *reinterpret_cast<const double*>(&v);
   }
-#pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j) {
-    if (j < k && lane == j) {
-      ids[(size_t)t * k + j] = sel_i[j];
-      w[(size_t)t * k + j] = (float)(ex[j] / S);
-    }
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = key_id(mine);
+    w[(size_t)t * k + lane] = (float)(ex / S);
   }
 }
 
@@ -126,12 +141,14 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
 
 // One workgroup: per-bucket running sums over chunks, then an exclusive scan over buckets.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __restrict__ chunk_cnt, int nchunks, int EL,
-                                                            int32_t* __restrict__ chunk_base,
+                                                            int bm, int32_t* __restrict__ chunk_base,
                                                             int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets) {
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ plan) {
   __shared__ int tot[2 * 1024 + 2];
+  __shared__ int mt[2 * 1024 + 2];
   const int NB = EL + 1;
-  for (int b = threadIdx.x; b < 2 * 1024; b += blockDim.x) tot[b] = 0;
+  for (int b = threadIdx.x; b < 2 * 1024; b += blockDim.x) tot[b] = mt[b] = 0;
   __syncthreads();
   for (int b = threadIdx.x; b < NB; b += blockDim.x) {
     int run = 0;
@@ -142,11 +159,14 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __res
       run += v;
     }
     tot[b] = run;
+    if (b < EL) mt[b] = (run + bm - 1) / bm;  // m-tiles of this expert
   }
   __syncthreads();
   block_exclusive_scan_2048(tot);  // tot[b] <- sum of tot[0..b)
+  block_exclusive_scan_2048(mt);
   for (int b = threadIdx.x; b < NB; b += blockDim.x) {
     offsets[b] = tot[b];
+    plan[b] = mt[b];
     if (b < EL) counts[b] = tot[b + 1] - tot[b];
   }
 }
@@ -208,17 +228,94 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __r
   }
 }
 
-hipError_t launch_permute(const int32_t* ids, int nslots, int e0, int EL, int32_t* chunk_cnt, int32_t* chunk_base,
-                          int32_t* counts, int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row,
-                          hipStream_t s) {
+// Everything in one workgroup when the slots are few (decode-sized calls): histogram,
+// scans, tile plan and the stable scatter, in rounds of 1024 slots.
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids, int nslots, int e0,
+                                                             int EL, int bm, int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ row_to_slot,
+                                                             int32_t* __restrict__ slot_to_row,
+                                                             int32_t* __restrict__ plan) {
+  __shared__ int a[2 * 1024 + 2];
+  __shared__ int mt[2 * 1024 + 2];
+  __shared__ int base[kPermSmallBuckets];
+  __shared__ int wcnt[16][kPermSmallBuckets];
   const int NB = EL + 1;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 2048; i += 1024) a[i] = mt[i] = 0;
+  for (int i = tid; i < 16 * kPermSmallBuckets; i += 1024) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int s = tid; s < nslots; s += 1024) atomicAdd(&a[bucket_of(ids[s], e0, EL)], 1);
+  __syncthreads();
+  for (int b = tid; b < EL; b += 1024) {
+    counts[b] = a[b];
+    mt[b] = (a[b] + bm - 1) / bm;
+  }
+  __syncthreads();
+  block_exclusive_scan_2048(a);
+  block_exclusive_scan_2048(mt);
+  for (int b = tid; b < NB; b += 1024) {
+    offsets[b] = a[b];
+    plan[b] = mt[b];
+    base[b] = a[b];
+  }
+  __syncthreads();
+  int nbits = 1;
+  while ((1 << nbits) < NB) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int r0 = 0; r0 < nslots; r0 += 1024) {
+    const int s = r0 + tid;
+    const bool valid = s < nslots;
+    const int b = valid ? bucket_of(ids[s], e0, EL) : 0;
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (b >> bit) & 1;
+      const uint64_t m = __ballot(valid && on);
+      match &= on ? m : ~m;
+    }
+    const int rank = __popcll(match & lt);
+    const int cnt = __popcll(match);
+    const bool leader = valid && rank == 0;
+    if (leader) wcnt[wave][b] = cnt;
+    __syncthreads();
+    int pos = 0;
+    if (valid) {
+      pos = base[b] + rank;
+      for (int q = 0; q < wave; ++q) pos += wcnt[q][b];
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&base[b], cnt);
+      wcnt[wave][b] = 0;
+    }
+    __syncthreads();
+    if (valid) {
+      if (b < EL) {
+        row_to_slot[pos] = s;
+        slot_to_row[s] = pos;
+      } else {
+        row_to_slot[pos] = -1;
+        slot_to_row[s] = -1;
+      }
+    }
+  }
+}
+
+hipError_t launch_permute(const int32_t* ids, int nslots, int e0, int EL, int32_t* chunk_cnt, int32_t* chunk_base,
+                          int32_t* counts, int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row, int bm,
+                          int32_t* plan, hipStream_t s) {
+  const int NB = EL + 1;
+  if (nslots <= kPermSmallSlots && NB <= kPermSmallBuckets) {
+    permute_small_kernel<<<1, 1024, 0, s>>>(ids, nslots, e0, EL, bm, counts, offsets, row_to_slot, slot_to_row, plan);
+    return hipGetLastError();
+  }
   const int nchunks = (nslots + kPermChunk - 1) / kPermChunk;
   if (nchunks > 0) {
     permute_hist_kernel<<<nchunks, 256, NB * sizeof(int), s>>>(ids, nslots, e0, EL, chunk_cnt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  permute_scan_kernel<<<1, 1024, 0, s>>>(chunk_cnt, nchunks, EL, chunk_base, counts, offsets);
+  permute_scan_kernel<<<1, 1024, 0, s>>>(chunk_cnt, nchunks, EL, bm, chunk_base, counts, offsets, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 0) return e;
   permute_scatter_kernel<<<nchunks, 256, 5 * NB * sizeof(int), s>>>(ids, nslots, e0, EL, chunk_base, offsets,

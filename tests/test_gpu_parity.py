@@ -40,6 +40,12 @@ def _small_cases():
         ("top1", synth.shrink(tiny, tokens=130, topk=1, seed=11)),
         ("k16_e1024", synth.shrink(tiny, tokens=40, num_experts=1024, local_begin=1000, num_local=24, topk=16,
                                    seed=12)),
+        # more than 16384 slots: chunked multi-workgroup permute
+        ("many_slots", synth.shrink(tiny, tokens=2100, hidden=256, inter=128, num_experts=64, num_local=16, topk=8,
+                                    seed=13)),
+        # more than 256 local experts: chunked permute as well
+        ("many_local", synth.shrink(tiny, tokens=96, hidden=256, inter=128, num_experts=1024, local_begin=100,
+                                    num_local=300, topk=8, seed=14)),
     ]
 
 
