@@ -53,11 +53,12 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream),
  *     do no host synchronisation and no allocation, so they may be captured in a
  *     HIP graph.  Calls on distinct workspaces may run concurrently.
- *   - Alignment: x, x_sf, w1, w2, h, logits, y and the workspace must be 16-byte
- *     aligned (the workspace 256-byte aligned).
+ *   - Alignment: x, x_sf, w1, w1_sf, w2, w2_sf, h, h_sf, logits and y must be
+ *     16-byte aligned, the workspace 256-byte aligned (MOE_ERR_MISALIGNED otherwise).
  *   - Limits: H and I multiples of 128 and at most 8192 (MOE_ERR_UNSUPPORTED above);
  *     1 <= E_loc <= E_tot <= 1024;
- *     1 <= k <= min(E_tot, 16); T*k < 2^31.
+ *     1 <= k <= min(E_tot, 16); T*k < 2^31; x smaller than 4 GiB (T*H < 2^32,
+ *     MOE_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MOE_EXPERT_LAYER_H_
 #define MOE_EXPERT_LAYER_H_

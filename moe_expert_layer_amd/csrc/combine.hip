@@ -15,6 +15,12 @@
 
 namespace moe {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // grid (ceil(H / 2048), min(T, 65535)): a workgroup owns 2048 columns of one token at a time
 // (tokens strided by the grid height); thread i handles columns 4i.. and 1024 + 4i.., so each
 // load instruction of the workgroup reads 4 KB of one Y2 row.  The token's slots are taken in
@@ -43,8 +49,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       for (int jj = 0; jj < 4; ++jj) {
         if (rows[jj] >= 0) {
           const float* src = y2 + (long long)rows[jj] * H + c0;
-          v0[jj] = *reinterpret_cast<const float4*>(src);
-          if (two) v1[jj] = *reinterpret_cast<const float4*>(src + 1024);
+          v0[jj] = ld_stream(src);  // Y2 is read once
+          if (two) v1[jj] = ld_stream(src + 1024);
         }
       }
 #pragma unroll

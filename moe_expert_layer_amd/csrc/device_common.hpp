@@ -66,6 +66,10 @@ __device__ __forceinline__ float inv_scale_of(int byte) {
   return __uint_as_float((uint32_t)(254 - byte) << 23);
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+// logistic function 1 / (1 + e^-z) from the hardware base-2 exponential and reciprocal
+// (a few ulp; the result is requantised to E4M3 right after)
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
 
 }  // namespace moe

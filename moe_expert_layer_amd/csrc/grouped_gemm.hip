@@ -93,7 +93,8 @@ struct Cfg {
   static_assert(WM * 2 == NW, "waves must cover the tile");
   static_assert(A_DMA >= 1 && B_DMA >= 1 && A_DMA * NW * 1024 == A_BYTES && B_DMA * NW * 1024 == B_BYTES, "");
   static_assert(WFMT == 0 || BN <= NW * 64, "one scale DMA per wave covers 64 weight rows");
-  static_assert(!PIPE || NSTAGE >= 3, "pipelined fragments need the next stage resident");
+  static_assert(PIPE != 1 || NSTAGE >= 3, "stage-ahead fragments need the next stage resident");
+  static_assert(PIPE != 2 || BK == 128, "the half-step pipeline splits 128-wide stages");
 };
 
 // Operand fragments of one stage for one wave (A rows, B columns, their scale bytes).
@@ -108,11 +109,23 @@ struct Frags {
 // ---------------------------------------------------------------------------------------
 // direct global -> LDS loads (the wave writes 64 lanes x 16 bytes at m0, lane order)
 
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+// the source is a uniform 64-bit base plus a 32-bit per-lane offset (the saddr form); the base
+// is passed through readfirstlane so it sits in SGPRs even where the compiler cannot prove it
+// uniform
+__device__ __forceinline__ const void* sbase(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  base = sbase(base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  base = sbase(base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
@@ -146,7 +159,7 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   using F = Frags<C::MI, C::NT, C::NH>;
   // LDS (dynamic, sized at launch): the stage ring, then the tile's activation scales
-  // [ks128][row] and FP8 weight scales [block][ks128].  The token list of the tile rows and
+  // [row][ks128] and FP8 weight scales [block][ks128].  The token list of the tile rows and
   // the epilogue's amax scratch live inside the ring while it is not in use.
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   uint8_t* ring = lds;
@@ -176,41 +189,63 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
   const int row_begin = g.offsets[e] + m_tile * BM;
   const int rows = min(BM, g.offsets[e + 1] - row_begin);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is made scalar for the 256-row tiles (fewer registers there); the 128-row
+  // tiles, whose row-tile skipping switches on it, allocate fewer with it left in a VGPR
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = BM == 256 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int wm = wave % C::WM, wn = wave / C::WM;
   const int nk = g.K / BK;       // stages
   const int nk128 = g.K / 128;   // scale steps
   const int n0 = MODE == 1 ? n_tile * 128 : n_tile * BN;
 
-  // ---- A row sources (token rows for FC1) and scales staged in LDS ----
+  // ---- tile rows: the token (FC1) or h row (FC2) of each tile row; rows past the expert's
+  //      last row repeat the first one ----
   for (int i = tid; i < BM; i += C::NTHR) {
     const int r = i < rows ? i : 0;
     s_tok[i] = MODE == 1 ? g.row_to_slot[row_begin + r] / g.k : row_begin + r;
   }
-  __syncthreads();
-  for (int i = tid; i < nk128 * BM; i += C::NTHR) {
-    const int ks = i / BM, r = i - ks * BM;
-    s_asf[i] = g.A_sf[(long long)s_tok[r] * nk128 + ks];
-  }
+  // FP8 weight scales of the tile's two 128-row blocks (FC1: gate n0/128 and up (I+n0)/128;
+  // FC2: n0/128 and n0/128 + 1, clamped), loaded now and written to LDS after the DMA issue
   const uint8_t* bsf_e = g.B_sf + (long long)e * g.bsf_estride;
-  if (WFMT == 0) {
-    // block rows: FC1 gate n0/128 and up (I+n0)/128; FC2 n0/128 and n0/128 + 1 (clamped)
-    for (int i = tid; i < 2 * nk128; i += C::NTHR) {
-      const int blk = i / nk128, ks = i - blk * nk128;
-      int br;
-      if (MODE == 1) br = blk == 0 ? n0 / 128 : (g.I + n0) / 128;
-      else br = min(n0 / 128 + blk, g.N / 128 - 1);
-      s_bsf[i] = bsf_e[(long long)br * nk128 + ks];
+  const bool bsf_mine = WFMT == 0 && tid < 2 * nk128;
+  int bsf_v = 0;
+  if (bsf_mine) {
+    const int blk = tid / nk128, ks = tid - blk * nk128;
+    const int br = MODE == 1 ? (blk == 0 ? n0 / 128 : (g.I + n0) / 128) : min(n0 / 128 + blk, g.N / 128 - 1);
+    bsf_v = bsf_e[(long long)br * nk128 + ks];
+  }
+  __syncthreads();
+  // activation scales of the tile rows in LDS as [row][k step]: moved by 4-byte DMA when a
+  // row is whole dwords (nk128 % 4 == 0), else by byte loads
+  const uint8_t* asf_gbase = MODE == 1 ? g.A_sf : g.A_sf + (long long)row_begin * nk128;
+  const bool asf_dma = (nk128 & 3) == 0;
+  constexpr int kAsfDma = (BM * kMaxKSteps / 256 + NW - 1) / NW;  // 64-lane DMAs per wave, at most
+  const int asf_n = BM * nk128 / 256;                               // 64-lane DMAs of the tile
+  uint32_t asf_off[kAsfDma];
+  if (asf_dma) {
+    const int dpr = nk128 / 4;  // dwords per row
+#pragma unroll
+    for (int j = 0; j < kAsfDma; ++j) {
+      const int q = (wave + NW * j) * 64 + lane, row = min(q / dpr, BM - 1);
+      asf_off[j] = (uint32_t)(s_tok[row] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)nk128 + (uint32_t)(q - row * dpr) * 4u;
+    }
+  } else {
+    for (int i = tid; i < nk128 * BM; i += C::NTHR) {
+      const int r = i / nk128;
+      s_asf[i] = asf_gbase[(long long)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * nk128 + (i - r * nk128)];
     }
   }
 
-  // ---- DMA sources of this lane, with the swizzled chunk folded in ----
-  const uint8_t* a_src[C::A_DMA];
+  // ---- DMA sources of this lane (offsets from uniform bases), swizzled chunk folded in ----
+  // FC1 gathers token rows of x (offsets below 2^32: x is smaller than 4 GiB); FC2 reads the
+  // tile's rows of h from the tile's first row
+  const uint8_t* a_gbase = MODE == 1 ? g.A : g.A + (long long)row_begin * g.K;
+  uint32_t a_off[C::A_DMA];
 #pragma unroll
   for (int j = 0; j < C::A_DMA; ++j) {
     const int r = (wave * C::A_DMA + j) * (64 / C::A_CPR) + lane / C::A_CPR;
     const int c = (lane % C::A_CPR) ^ swz<C::A_CPR>(r);
-    a_src[j] = g.A + (long long)s_tok[r] * g.K + c * 16;
+    a_off[j] = (uint32_t)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)g.K + (uint32_t)(c * 16);
   }
   const uint8_t* b_e = g.B + (long long)e * g.b_estride;
   auto b_row = [&](int n) -> int {
@@ -218,35 +253,41 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
     const int rr = n0 + n;
     return rr < g.N ? rr : g.N - 1;
   };
-  const long long b_ld = WFMT == 0 ? g.K : g.K / 2;
-  const uint8_t* b_src[C::B_DMA];
+  const uint32_t b_ld = WFMT == 0 ? g.K : g.K / 2;
+  uint32_t b_off[C::B_DMA];
 #pragma unroll
   for (int j = 0; j < C::B_DMA; ++j) {
     const int n = (wave * C::B_DMA + j) * (64 / C::B_CPR) + lane / C::B_CPR;
     const int c = (lane % C::B_CPR) ^ swz<C::B_CPR>(n);
-    b_src[j] = b_e + (long long)b_row(n) * b_ld + c * 16;
+    b_off[j] = (uint32_t)b_row(n) * b_ld + (uint32_t)(c * 16);
   }
   // MXFP4: wave w loads the scale dword (4 blocks of 32 = one 128-wide K step) of weight rows
   // (w % (BN/64)) * 64 + lane; waves beyond BN/64 load a second copy that is never read
-  const uint8_t* s_src = nullptr;
-  if (WFMT == 1) s_src = bsf_e + (long long)b_row((wave % (BN / 64)) * 64 + lane) * (g.K / 32);
+  uint32_t s_off = 0;
+  if (WFMT == 1) s_off = (uint32_t)b_row((wave % (BN / 64)) * 64 + lane) * (uint32_t)(g.K / 32);
   __syncthreads();  // s_tok (inside the ring) is consumed before the ring is filled
+  if (asf_dma) {
+#pragma unroll
+    for (int j = 0; j < kAsfDma; ++j)
+      if (wave + NW * j < asf_n) dma4(asf_gbase, asf_off[j], uniform(lds_addr(s_asf) + (wave + NW * j) * 256));
+  }
 
   const uint32_t ring0 = lds_addr(ring);
   auto issue = [&](int ks) {
     const uint32_t st = ring0 + (uint32_t)((ks % NSTAGE) * C::STAGE);
+    const uint8_t* ab = a_gbase + (long long)ks * C::A_ROWB;
+    const uint8_t* bb = b_e + (long long)ks * C::B_ROWB;
 #pragma unroll
-    for (int j = 0; j < C::A_DMA; ++j)
-      dma16(a_src[j] + (long long)ks * C::A_ROWB, uniform(st + (wave * C::A_DMA + j) * 1024));
+    for (int j = 0; j < C::A_DMA; ++j) dma16(ab, a_off[j], uniform(st + (wave * C::A_DMA + j) * 1024));
 #pragma unroll
-    for (int j = 0; j < C::B_DMA; ++j)
-      dma16(b_src[j] + (long long)ks * C::B_ROWB, uniform(st + C::A_BYTES + (wave * C::B_DMA + j) * 1024));
+    for (int j = 0; j < C::B_DMA; ++j) dma16(bb, b_off[j], uniform(st + C::A_BYTES + (wave * C::B_DMA + j) * 1024));
     if (WFMT == 1)
-      dma4(s_src + ((ks * BK) / 128) * 4, uniform(st + C::A_BYTES + C::B_BYTES + wave * 256));
+      dma4(bsf_e + ((ks * BK) / 128) * 4, s_off, uniform(st + C::A_BYTES + C::B_BYTES + wave * 256));
   };
   // wait until at most `ahead` stages of this wave's DMA are in flight, then workgroup barrier
   auto wait_stages = [&](int ahead) {
-    if (ahead >= 2) wait_vm_barrier<2 * C::PER_STAGE>();
+    if (ahead >= 3) wait_vm_barrier<3 * C::PER_STAGE>();
+    else if (ahead == 2) wait_vm_barrier<2 * C::PER_STAGE>();
     else if (ahead == 1) wait_vm_barrier<C::PER_STAGE>();
     else wait_vm_barrier<0>();
   };
@@ -263,58 +304,80 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
   // a wave whose rows all lie past the expert's last row skips its MFMAs (decode-sized experts);
   // the test is wave-uniform so the MFMA burst stays one straight-line block
   const bool wave_live = wm * WTM < rows;
-  // first weight row (tile-local) of column tile ct of this wave
-  auto bcol = [&](int ct) -> int {
-    if (MODE == 1) return ct < C::NT / 2 ? wn * 64 + ct * 32 : 128 + wn * 64 + (ct - C::NT / 2) * 32;
-    return wn * (BN / 2) + ct * 32;
+  // first weight row (tile-local) of column tile ct of this wave, and its offset from tile 0's
+  auto bdelta = [](int ct) -> int {
+    if (MODE == 1) return ct < C::NT / 2 ? ct * 32 : 128 + (ct - C::NT / 2) * 32;
+    return ct * 32;
   };
+  const int bcol0 = MODE == 1 ? wn * 64 : wn * (BN / 2);
+  auto bcol = [&](int ct) -> int { return bcol0 + bdelta(ct); };
 
-  // operand fragments of stage ks from its ring slot
-  auto load = [&](int ks, F& f) {
+  // LDS read addresses.  Rows 32 apart have the same swizzle in 64- and 32-byte rows and
+  // differ only in bit 2 of it in 128-byte rows, where bit 2 of the chunk index is the 64-wide
+  // K half; so every operand read is a per-lane base (row tile 0, K half 0), possibly with
+  // byte 64 (FP8) or 32 (FP4) toggled, plus an immediate row offset.
+  const int ra = wm * WTM + lrow, rb = bcol0 + lrow;
+  uint32_t a_lds[2], b_lds[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    a_lds[hi] = ra * C::A_ROWB + (((2 * hi + kb) ^ swz<C::A_CPR>(ra)) << 4);
+    b_lds[hi] = WFMT == 0 ? rb * C::B_ROWB + (((2 * hi + kb) ^ swz<C::B_CPR>(rb)) << 4)
+                           : rb * C::B_ROWB + ((kb ^ swz<C::B_CPR>(rb)) << 4);
+  }
+
+  // operand fragments of 64-wide K steps h0 .. h0 + NHF - 1 of stage ks from its ring slot
+  auto load_into = [&](int ks, int h0, auto& f) {
+    constexpr int NHF = sizeof(f.b) / sizeof(f.b[0]);
     const uint8_t* st = ring + (ks % NSTAGE) * C::STAGE;
-    const uint8_t* sa_ = st;
     const uint8_t* sb_ = st + C::A_BYTES;
     const int k128 = (ks * BK) / 128;
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) f.sa[mi] = s_asf[k128 * BM + wm * WTM + mi * 32 + lrow];
+    for (int mi = 0; mi < C::MI; ++mi) f.sa[mi] = s_asf[(ra + mi * 32) * nk128 + k128];
     int sbu0 = 0, sbu1 = 0;
-    if (WFMT == 0) {
+    if (WFMT == 0) {  // one weight scale per 128x128 block
       if (MODE == 1) { sbu0 = s_bsf[k128]; sbu1 = s_bsf[nk128 + k128]; }
       else { sbu0 = s_bsf[(BN == 256 ? wn : 0) * nk128 + k128]; sbu1 = sbu0; }
     }
 #pragma unroll
-    for (int h = 0; h < C::NH; ++h) {
+    for (int hh = 0; hh < NHF; ++hh) {
+      const int h = h0 + hh;
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi) {
-        const int r = wm * WTM + mi * 32 + lrow;
-        const uint4 lo = lds16(sa_ + r * C::A_ROWB + (((4 * h + kb) ^ swz<C::A_CPR>(r)) << 4));
-        const uint4 hi = lds16(sa_ + r * C::A_ROWB + (((4 * h + 2 + kb) ^ swz<C::A_CPR>(r)) << 4));
-        f.a[h][mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const bool flip = C::A_CPR == 8 && ((h ^ mi) & 1);
+        const int imm = mi * 32 * C::A_ROWB;
+        const uint4 lo = lds16(st + (flip ? a_lds[0] ^ 64u : a_lds[0]) + imm);
+        const uint4 hi = lds16(st + (flip ? a_lds[1] ^ 64u : a_lds[1]) + imm);
+        f.a[hh][mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
       for (int ct = 0; ct < C::NT; ++ct) {
-        const int n = bcol(ct) + lrow;
+        const int d = bdelta(ct);
         if (WFMT == 0) {
-          const uint4 lo = lds16(sb_ + n * C::B_ROWB + (((4 * h + kb) ^ swz<C::B_CPR>(n)) << 4));
-          const uint4 hi = lds16(sb_ + n * C::B_ROWB + (((4 * h + 2 + kb) ^ swz<C::B_CPR>(n)) << 4));
-          f.b[h][ct] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          f.sb[h][ct] = (MODE == 1 && ct >= C::NT / 2) ? sbu1 : sbu0;
+          const bool flip = C::B_CPR == 8 && ((h ^ (d / 32)) & 1);
+          const int imm = d * C::B_ROWB;
+          const uint4 lo = lds16(sb_ + (flip ? b_lds[0] ^ 64u : b_lds[0]) + imm);
+          const uint4 hi = lds16(sb_ + (flip ? b_lds[1] ^ 64u : b_lds[1]) + imm);
+          f.b[hh][ct] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          f.sb[hh][ct] = (MODE == 1 && ct >= C::NT / 2) ? sbu1 : sbu0;
         } else {
-          const uint4 q = lds16(sb_ + n * C::B_ROWB + (((2 * h + kb) ^ swz<C::B_CPR>(n)) << 4));
-          f.b[h][ct] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-          const int dw = *reinterpret_cast<const int*>(st + C::A_BYTES + C::B_BYTES + n * 4);
+          // chunk 2h + kb of a 64-byte row (bit 1 = K half) or chunk kb of a 32-byte row
+          const bool flip = C::B_CPR == 4 && (h & 1);
+          const uint4 q = lds16(sb_ + (flip ? b_lds[0] ^ 32u : b_lds[0]) + d * C::B_ROWB);
+          f.b[hh][ct] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          const int dw = *reinterpret_cast<const int*>(st + C::A_BYTES + C::B_BYTES + rb * 4 + d * 4);
           const int blk = ((ks * BK) % 128) / 32 + 2 * h + kb;  // 32-wide block inside the 128-wide step
-          f.sb[h][ct] = (dw >> (8 * blk)) & 0xff;
+          f.sb[hh][ct] = dw >> (8 * blk);                         // the MFMA reads the low byte
         }
       }
     }
   };
   // MFMAs of one stage for the first NL row tiles of the wave (row tiles past the expert's last
   // row are skipped; NL is wave-uniform, so each case is one straight-line MFMA burst)
-  auto mma_n = [&](const F& f, auto nl) {
+  auto mma_n = [&](const auto& f, auto nl) {
     constexpr int NL = decltype(nl)::value;
+    constexpr int NHF = sizeof(f.b) / sizeof(f.b[0]);
 #pragma unroll
-    for (int h = 0; h < C::NH; ++h)
+    for (int h = 0; h < NHF; ++h)
 #pragma unroll
       for (int ct = 0; ct < C::NT; ++ct)
 #pragma unroll
@@ -324,37 +387,38 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
                                                                         f.sb[h][ct]);
   };
   const int live_tiles = min(C::MI, max(0, (rows - wm * WTM + 31) / 32));
-  auto mma = [&](const F& f) {
+  auto mma = [&](const auto& f) {
     if (BM != 128 || live_tiles >= C::MI) mma_n(f, std::integral_constant<int, C::MI>{});  // 128-row tiles only
     else if (C::MI > 1 && live_tiles == 1) mma_n(f, std::integral_constant<int, 1>{});
     else if (C::MI > 2 && live_tiles == 2) mma_n(f, std::integral_constant<int, (C::MI > 2 ? 2 : 1)>{});
     else if (C::MI > 3 && live_tiles == 3) mma_n(f, std::integral_constant<int, (C::MI > 3 ? 3 : 1)>{});
   };
 
-  // prologue: NSTAGE-1 stages in flight
+  // prologue: NSTAGE-1 stages in flight (the first wait's barrier also publishes s_bsf)
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < nk) issue(s);
+  if (bsf_mine) s_bsf[tid] = (uint8_t)bsf_v;
 
-  if (!PIPE) {
+  if (PIPE == 0) {
     for (int ks = 0; ks < nk; ++ks) {
       wait_stages(min(nk - 1 - ks, NSTAGE - 2));
       if (ks + NSTAGE - 1 < nk) issue(ks + NSTAGE - 1);
       if (!wave_live) continue;
       F f;
-      load(ks, f);
+      load_into(ks, 0, f);
       mma(f);
     }
-  } else {
+  } else if (PIPE == 1) {
     // stage ks+1 must be resident while stage ks multiplies: one stage less of DMA lookahead
     F f0, f1;
     wait_stages(min(nk - 1, NSTAGE - 2));
-    if (wave_live) load(0, f0);
+    if (wave_live) load_into(0, 0, f0);
     auto step = [&](int ks, F& cur, F& nxt) {
       if (ks + 1 < nk) {
         wait_stages(min(nk - 2 - ks, NSTAGE - 3));
         if (ks + NSTAGE - 1 < nk) issue(ks + NSTAGE - 1);
-        if (wave_live) load(ks + 1, nxt);
+        if (wave_live) load_into(ks + 1, 0, nxt);
       }
       if (wave_live) mma(cur);
     };
@@ -362,10 +426,43 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
       step(ks, f0, f1);
       if (ks + 1 < nk) step(ks + 1, f1, f0);
     }
+  } else {
+    // half-step pipeline (two 64-wide K steps per stage): the fragments of the next half are
+    // read from LDS while the MFMAs of the current one run.  The stage boundary (DMA wait,
+    // barrier, next DMA issue) sits between a stage's second-half reads and its MFMAs, when
+    // every wave is done reading the stage, so the ring holds NSTAGE stages with NSTAGE - 1
+    // of them in flight.
+    static_assert(PIPE != 2 || C::NH == 2, "half-step pipeline needs 128-wide stages");
+    using FH = Frags<C::MI, C::NT, 1>;
+    FH x, y;
+    if (NSTAGE - 1 < nk) issue(NSTAGE - 1);
+    wait_stages(min(nk - 1, NSTAGE - 1));
+    // every part of the loop is straight-line code so the reads of one half and the MFMAs of
+    // the other interleave freely; waves with no live rows only take part in the DMA and barriers
+    auto run = [&](auto live) {
+      constexpr bool L = decltype(live)::value;
+      if (L) load_into(0, 0, x);
+      int ks = 0;
+      for (; ks + NSTAGE < nk; ++ks) {  // steady state: stage ks + NSTAGE goes to the freed slot
+        if (L) { load_into(ks, 1, y); mma(x); }
+        wait_stages(NSTAGE - 2);
+        issue(ks + NSTAGE);
+        if (L) { load_into(ks + 1, 0, x); mma(y); }
+      }
+      for (; ks + 1 < nk; ++ks) {  // drain
+        if (L) { load_into(ks, 1, y); mma(x); }
+        wait_stages(nk - 2 - ks);
+        if (L) { load_into(ks + 1, 0, x); mma(y); }
+      }
+      if (L) { load_into(ks, 1, y); mma(x); mma(y); }
+    };
+    if (wave_live) run(std::true_type{});
+    else run(std::false_type{});
   }
 
   if (MODE == 2) {
-    // ---- FC2 epilogue: fp32 rows of Y2 (32 consecutive columns per lane group) ----
+    // ---- FC2 epilogue: fp32 rows of Y2 (32 consecutive columns per lane group), stored
+    //      non-temporally so the burst at the end of the tiles does not evict the operands ----
     if (wave_live) {
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi)
@@ -377,7 +474,7 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
 #pragma unroll
             for (int ct = 0; ct < C::NT; ++ct) {
               const int col = n0 + bcol(ct) + lrow;
-              if (col < g.N) dst[col] = acc[mi][ct][i];
+              if (col < g.N) __builtin_nontemporal_store(acc[mi][ct][i], dst + col);  // read once, by the combine
             }
           }
         }
@@ -405,6 +502,15 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
         }
         acc[mi][c][i] = hh;  // h overwrites the gate accumulator
       }
+  // amax of each tile row over the wave's 64 columns: a DPP max within each 16-lane row
+  // (quad swaps, then rotations by 4 and 8), then row 1 (3) takes row 0's (2's) result through
+  // row_bcast:15, so lanes 16-31 and 48-63 hold the maximum over their 32-lane half
+  auto max_dpp = [](float m, auto ctrl, auto row_mask) -> float {
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), decltype(ctrl)::value,
+                                              decltype(row_mask)::value, 0xf, false);
+    return fmaxf(m, __int_as_float(o));
+  };
+  using all_rows = std::integral_constant<int, 0xf>;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -412,12 +518,20 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
       float m = 0.f;
 #pragma unroll
       for (int c = 0; c < NC; ++c) m = fmaxf(m, fabsf(acc[mi][c][i]));
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-      if (lrow == 0) s_amax[wn][wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3)] = m;
+      m = max_dpp(m, std::integral_constant<int, 0xB1>{}, all_rows{});   // quad_perm [1,0,3,2]
+      m = max_dpp(m, std::integral_constant<int, 0x4E>{}, all_rows{});   // quad_perm [2,3,0,1]
+      m = max_dpp(m, std::integral_constant<int, 0x124>{}, all_rows{});  // row_ror 4
+      m = max_dpp(m, std::integral_constant<int, 0x128>{}, all_rows{});  // row_ror 8
+      m = max_dpp(m, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});  // row_bcast 15
+      if (lrow == 31) s_amax[wn][wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3)] = m;
     }
   __syncthreads();  // every wave is past its last ring read; s_amax complete
-  uint8_t* stage_h = ring;  // [BM rows][128 B] code tile
+  // E4M3 codes: lanes 4q..4q+3 hold 4 consecutive columns of a row; lane 4q gathers them
+  // (quad_perm broadcasts) and writes one dword of the [BM rows][128 B] code tile
+  uint8_t* stage_h = ring;
+  auto from_lane = [](int v, auto ctrl) -> int {
+    return __builtin_amdgcn_update_dpp(v, v, decltype(ctrl)::value, 0xf, 0xf, false);
+  };
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -429,7 +543,10 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int code = __builtin_amdgcn_cvt_pk_fp8_f32(acc[mi][c][i] * inv, 0.0f, 0, false) & 0xff;
-        stage_h[r * 128 + wn * 64 + c * 32 + lrow] = (uint8_t)code;
+        const int word = code | (from_lane(code, std::integral_constant<int, 0x55>{}) << 8) |
+                         (from_lane(code, std::integral_constant<int, 0xAA>{}) << 16) |
+                         (from_lane(code, std::integral_constant<int, 0xFF>{}) << 24);
+        if ((lrow & 3) == 0) *reinterpret_cast<int*>(stage_h + r * 128 + wn * 64 + c * 32 + lrow) = word;
       }
       if (wn == 0 && lrow == 0 && r < rows) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = (uint8_t)byte;
     }
@@ -485,8 +602,8 @@ static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
 template <int MODE>
 static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_t grid, hipStream_t s) {
   if (variant == 1) {
-    return wfmt == 0 ? launch_one<MODE, 0, 256, 256, 128, 2, 8, 64, 0>(a, grid, s)
-                     : launch_one<MODE, 1, 256, 256, 128, 2, 8, 64, 0>(a, grid, s);
+    return wfmt == 0 ? launch_one<MODE, 0, 256, 256, 128, 2, 8, 64, 2>(a, grid, s)
+                     : launch_one<MODE, 1, 256, 256, 128, 2, 8, 64, 2>(a, grid, s);
   }
   // small experts: two workgroups fit one CU (<= 80 KB of LDS each) so one streams weights
   // while the other is in its prologue or epilogue; FC2 tiles are 128 columns wide

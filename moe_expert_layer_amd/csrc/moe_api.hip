@@ -107,6 +107,9 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->variant < -1 || d->variant > 1) return fail(MOE_ERR_INVALID_DESC, "variant %d unknown", d->variant);
   if (!moe::gemm_supports(d->hidden, d->inter))
     return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d above the supported 8192", d->hidden, d->inter);
+  if ((long long)d->num_tokens * d->hidden >= (1LL << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "x of num_tokens * hidden = %lld bytes is 4 GiB or more",
+                (long long)d->num_tokens * d->hidden);
   return MOE_OK;
 }
 

@@ -110,3 +110,14 @@ def test_zero_tokens_is_a_noop_without_device(L):
     d = B.desc_from_workload(synth.shrink(synth.workload("tiny"), tokens=0))
     assert L.moe_layer(ctypes.byref(d), *([None] * 15), 0, None) == B.MOE_OK
     assert L.moe_route_permute(ctypes.byref(d), *([None] * 7), None, 0, None) == B.MOE_OK
+
+
+def test_oversized_activation_matrix_unsupported(L):
+    # the FC1 loads address x with 32-bit offsets: T * H must stay below 2^32 bytes
+    d = B.desc_from_workload(synth.workload("decode"))
+    n = ctypes.c_size_t(0)
+    d.num_tokens = (1 << 32) // d.hidden + 1
+    d.topk = 1
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED
+    d.num_tokens = (1 << 32) // d.hidden - 1
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_OK
