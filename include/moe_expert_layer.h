@@ -101,7 +101,8 @@ typedef struct {
   float act_clamp;        /* OAI only: gate <= clamp, |up| <= clamp; +inf = no clamp (must be > 0) */
   float act_alpha;        /* OAI only: sigmoid(alpha * gate); default 1.0 */
   float act_up_bias;      /* OAI only: (up + up_bias); default 0.0 */
-  int32_t variant;        /* GEMM tiles: -1 = heuristic; 0 = 128-row tiles; 1 = 256-row tiles */
+  int32_t variant;        /* GEMM tiles: -1 = heuristic; 0 = 128-row tiles; 1 = 256-row tiles;
+                             2 = 32-row tiles */
 } moe_layer_desc;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION at build time). */

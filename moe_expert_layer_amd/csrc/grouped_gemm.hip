@@ -33,6 +33,7 @@
 // expert on one XCD, sharing its L2).  Waves whose rows all lie past an expert's last row
 // skip their MFMAs (decode-sized experts).
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -70,12 +71,13 @@ struct GemmArgs {
 };
 
 // Tile shape: BM rows x BN weight rows, K advancing BK per stage through an NSTAGE ring,
-// NW waves arranged (BM/WTM) x 2, each wave WTM rows x BN/2 weight rows.  PIPE: the operand
+// NW waves arranged (BM/WTM) x WN, each wave WTM rows x BN/WN weight rows.  PIPE: the operand
 // fragments of stage ks+1 are read from LDS while the MFMAs of stage ks run.
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
 struct Cfg {
   static constexpr int NTHR = NW * 64;
   static constexpr int WM = BM / WTM;                       // waves along M
+  static constexpr int WN = NW / WM;                        // waves along N
   static constexpr int MI = WTM / 32;                       // 32-row tiles per wave
   static constexpr int A_ROWB = BK;                         // bytes per activation row per stage
   static constexpr int B_ROWB = WFMT == 0 ? BK : BK / 2;    // bytes per weight row per stage
@@ -83,15 +85,19 @@ struct Cfg {
   static constexpr int B_BYTES = BN * B_ROWB;
   static constexpr int S_BYTES = WFMT == 1 ? NW * 256 : 0;  // MXFP4 scale dwords (64 rows per wave)
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int A_DMA = A_BYTES / 1024 / NW;         // 16-byte DMA instructions per wave per stage
+  static constexpr int A_INSTR = A_BYTES / 1024;            // 1 KB DMA instructions of the A tile per stage
+  // per wave and stage; a tile of fewer instructions than waves is loaded by every wave, wave w
+  // repeating instruction w % A_INSTR (same bytes, same place), so all waves count alike
+  static constexpr int A_DMA = A_INSTR >= NW ? A_INSTR / NW : 1;
   static constexpr int B_DMA = B_BYTES / 1024 / NW;
   static constexpr int S_DMA = WFMT == 1 ? 1 : 0;           // 4-byte DMA instructions per wave per stage
   static constexpr int PER_STAGE = A_DMA + B_DMA + S_DMA;
-  static constexpr int NT = BN / 2 / 32;                    // 32-wide column tiles per wave
+  static constexpr int NT = BN / WN / 32;                   // 32-wide column tiles per wave
   static constexpr int NH = BK / 64;                        // 64-wide MFMA K steps per stage
   static constexpr int A_CPR = A_ROWB / 16, B_CPR = B_ROWB / 16;  // 16-byte chunks per row
-  static_assert(WM * 2 == NW, "waves must cover the tile");
-  static_assert(A_DMA >= 1 && B_DMA >= 1 && A_DMA * NW * 1024 == A_BYTES && B_DMA * NW * 1024 == B_BYTES, "");
+  static_assert(WM * WN == NW && NT >= 1 && (MODE == 2 || NT % 2 == 0), "waves must cover the tile");
+  static_assert(A_INSTR >= 1 && B_DMA >= 1 && B_DMA * NW * 1024 == B_BYTES, "");
+  static_assert(A_INSTR >= NW ? A_DMA * NW == A_INSTR : NW % A_INSTR == 0, "");
   static_assert(WFMT == 0 || BN <= NW * 64, "one scale DMA per wave covers 64 weight rows");
   static_assert(PIPE != 1 || NSTAGE >= 3, "stage-ahead fragments need the next stage resident");
   static_assert(PIPE != 2 || BK == 128, "the half-step pipeline splits 128-wide stages");
@@ -155,7 +161,7 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ plan, int
 }
 
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
-__global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   using F = Frags<C::MI, C::NT, C::NH>;
   // LDS (dynamic, sized at launch): the stage ring, then the tile's activation scales
@@ -169,7 +175,31 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
   int* s_tok = reinterpret_cast<int*>(ring + NSTAGE * C::STAGE - BM * 4);  // prologue only
   float(*s_amax)[BM] = reinterpret_cast<float(*)[BM]>(ring + BM * 128);      // epilogue only
 
-  const int total = g.plan[g.EL] * g.n_tiles;
+  // tile plan: plan[e] = m-tiles of the experts before e, plan[EL] = all.  The fused path
+  // passes the one the permute wrote; the split entry points pass none and every workgroup
+  // scans the offsets itself (into the ring, which the prologue does not use yet)
+  const int32_t* plan = g.plan;
+  if (plan == nullptr) {
+    int* s_plan = reinterpret_cast<int*>(ring);  // [EL + 1]
+    int* s_wsum = s_plan + kMaxExperts + 8;      // [NW]
+    const int t = threadIdx.x, n = g.EL + 1, per = (n + C::NTHR - 1) / C::NTHR, beg = t * per;
+    int sum = 0;
+    for (int j = 0; j < per; ++j) {
+      const int ee = beg + j;
+      if (ee < n) s_plan[ee] = sum;
+      if (ee < g.EL) sum += (g.offsets[ee + 1] - g.offsets[ee] + BM - 1) / BM;
+    }
+    const int inc = wave_inclusive_scan(sum);
+    if ((t & 63) == 63) s_wsum[t >> 6] = inc;
+    __syncthreads();
+    int base = inc - sum;
+    for (int w = 0; w < (t >> 6); ++w) base += s_wsum[w];
+    for (int j = 0; j < per; ++j)
+      if (beg + j < n) s_plan[beg + j] += base;
+    __syncthreads();
+    plan = s_plan;
+  }
+  const int total = plan[g.EL] * g.n_tiles;
   const int bid = blockIdx.x;
   if (bid >= total) return;
   int L;  // XCD-aware order: dispatch is round-robin over 8 XCDs; each XCD gets a contiguous range
@@ -177,9 +207,9 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
     const int x = bid & 7, p = bid >> 3, q = total >> 3, r = total & 7;
     L = x * q + (x < r ? x : r) + p;
   }
-  const int e = find_expert(g.plan, g.EL, L / g.n_tiles);
-  const int mt_e = g.plan[e + 1] - g.plan[e];
-  const int li = L - g.plan[e] * g.n_tiles;
+  const int e = find_expert(plan, g.EL, L / g.n_tiles);
+  const int mt_e = plan[e + 1] - plan[e];
+  const int li = L - plan[e] * g.n_tiles;
   const int gn = g.n_tiles < kGroupN ? g.n_tiles : kGroupN;
   const int grp = li / (gn * mt_e);
   const int gsz = (g.n_tiles - grp * gn) < gn ? (g.n_tiles - grp * gn) : gn;
@@ -218,7 +248,7 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
   // activation scales of the tile rows in LDS as [row][k step]: moved by 4-byte DMA when a
   // row is whole dwords (nk128 % 4 == 0), else by byte loads
   const uint8_t* asf_gbase = MODE == 1 ? g.A_sf : g.A_sf + (long long)row_begin * nk128;
-  const bool asf_dma = (nk128 & 3) == 0;
+  const bool asf_dma = (nk128 & 3) == 0 && ((BM * nk128) & 255) == 0;
   constexpr int kAsfDma = (BM * kMaxKSteps / 256 + NW - 1) / NW;  // 64-lane DMAs per wave, at most
   const int asf_n = BM * nk128 / 256;                               // 64-lane DMAs of the tile
   uint32_t asf_off[kAsfDma];
@@ -243,7 +273,7 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
   uint32_t a_off[C::A_DMA];
 #pragma unroll
   for (int j = 0; j < C::A_DMA; ++j) {
-    const int r = (wave * C::A_DMA + j) * (64 / C::A_CPR) + lane / C::A_CPR;
+    const int r = ((wave * C::A_DMA + j) % C::A_INSTR) * (64 / C::A_CPR) + lane / C::A_CPR;
     const int c = (lane % C::A_CPR) ^ swz<C::A_CPR>(r);
     a_off[j] = (uint32_t)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)g.K + (uint32_t)(c * 16);
   }
@@ -278,7 +308,8 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
     const uint8_t* ab = a_gbase + (long long)ks * C::A_ROWB;
     const uint8_t* bb = b_e + (long long)ks * C::B_ROWB;
 #pragma unroll
-    for (int j = 0; j < C::A_DMA; ++j) dma16(ab, a_off[j], uniform(st + (wave * C::A_DMA + j) * 1024));
+    for (int j = 0; j < C::A_DMA; ++j)
+      dma16(ab, a_off[j], uniform(st + ((wave * C::A_DMA + j) % C::A_INSTR) * 1024));
 #pragma unroll
     for (int j = 0; j < C::B_DMA; ++j) dma16(bb, b_off[j], uniform(st + C::A_BYTES + (wave * C::B_DMA + j) * 1024));
     if (WFMT == 1)
@@ -309,7 +340,7 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
     if (MODE == 1) return ct < C::NT / 2 ? ct * 32 : 128 + (ct - C::NT / 2) * 32;
     return ct * 32;
   };
-  const int bcol0 = MODE == 1 ? wn * 64 : wn * (BN / 2);
+  const int bcol0 = MODE == 1 ? wn * (128 / C::WN) : wn * (BN / C::WN);
   auto bcol = [&](int ct) -> int { return bcol0 + bdelta(ct); };
 
   // LDS read addresses.  Rows 32 apart have the same swizzle in 64- and 32-byte rows and
@@ -336,7 +367,7 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
     int sbu0 = 0, sbu1 = 0;
     if (WFMT == 0) {  // one weight scale per 128x128 block
       if (MODE == 1) { sbu0 = s_bsf[k128]; sbu1 = s_bsf[nk128 + k128]; }
-      else { sbu0 = s_bsf[(BN == 256 ? wn : 0) * nk128 + k128]; sbu1 = sbu0; }
+      else { sbu0 = s_bsf[(wn * (BN / C::WN)) / 128 * nk128 + k128]; sbu1 = sbu0; }
     }
 #pragma unroll
     for (int hh = 0; hh < NHF; ++hh) {
@@ -483,100 +514,142 @@ __global__ __launch_bounds__(NW * 64, BM == 128 ? 2 : 1) void grouped_gemm_kerne
   }
 
   // ---- FC1 epilogue: activation, 1x128 amax, UE8M0 scale, E4M3 codes ----
-  // lane holds rows 8*(i/4) + 4*kb + i%4 of each row tile; h column wn*64 + c*32 + lrow (c = 0, 1)
+  // lane holds rows 8*(i/4) + 4*kb + i%4 of each row tile; h column wn*128/WN + c*32 + lrow.
+  // Each step runs over all of the lane's values as straight-line code, with the LDS writes
+  // of a step gathered under one lane mask, so independent chains interleave.
   constexpr int NC = C::NT / 2;
+  // row of value i of row tile mi relative to the lane's first row (a compile-time constant)
+  auto drow = [](int mi, int i) { return mi * 32 + 8 * (i >> 2) + (i & 3); };
+  const int row0 = wm * WTM + 4 * kb;
+  if (g.act == 1) {
+    const float cl = g.clamp, al = g.alpha, bi = g.bias;
 #pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float gt = acc[mi][c][i], up = acc[mi][c + NC][i];
-        float hh;
-        if (g.act == 1) {
-          gt = fminf(gt, g.clamp);
-          up = fminf(fmaxf(up, -g.clamp), g.clamp);
-          hh = gt * sigmoidf_(g.alpha * gt) * (up + g.bias);
-        } else {
-          hh = gt * sigmoidf_(gt) * up;
+        for (int i = 0; i < 16; ++i) {  // clamps as one med3 each; h overwrites the gate
+          const float gt = __builtin_amdgcn_fmed3f(acc[mi][c][i], -INFINITY, cl);
+          const float up = __builtin_amdgcn_fmed3f(acc[mi][c + NC][i], -cl, cl);
+          acc[mi][c][i] = gt * sigmoidf_(al * gt) * (up + bi);
         }
-        acc[mi][c][i] = hh;  // h overwrites the gate accumulator
-      }
-  // amax of each tile row over the wave's 64 columns: a DPP max within each 16-lane row
-  // (quad swaps, then rotations by 4 and 8), then row 1 (3) takes row 0's (2's) result through
-  // row_bcast:15, so lanes 16-31 and 48-63 hold the maximum over their 32-lane half
-  auto max_dpp = [](float m, auto ctrl, auto row_mask) -> float {
-    const int o = __builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), decltype(ctrl)::value,
-                                              decltype(row_mask)::value, 0xf, false);
-    return fmaxf(m, __int_as_float(o));
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float gt = acc[mi][c][i];
+          acc[mi][c][i] = gt * sigmoidf_(gt) * acc[mi][c + NC][i];
+        }
+  }
+  // amax of each tile row over the wave's columns, as an unsigned max of the (non-negative)
+  // float bits: a DPP max within each 16-lane row (quad swaps, then rotations by 4 and 8),
+  // then row 1 (3) takes row 0's (2's) result through row_bcast:15, so lanes 16-31 and 48-63
+  // hold the maximum over their 32-lane half
+  auto max_dpp = [](uint32_t m, auto ctrl, auto row_mask) -> uint32_t {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, decltype(ctrl)::value,
+                                                             decltype(row_mask)::value, 0xf, false);
+    return m > o ? m : o;
   };
   using all_rows = std::integral_constant<int, 0xf>;
+  uint32_t am[C::MI][16];
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float m = 0.f;
+      uint32_t m = 0;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) m = fmaxf(m, fabsf(acc[mi][c][i]));
-      m = max_dpp(m, std::integral_constant<int, 0xB1>{}, all_rows{});   // quad_perm [1,0,3,2]
-      m = max_dpp(m, std::integral_constant<int, 0x4E>{}, all_rows{});   // quad_perm [2,3,0,1]
-      m = max_dpp(m, std::integral_constant<int, 0x124>{}, all_rows{});  // row_ror 4
-      m = max_dpp(m, std::integral_constant<int, 0x128>{}, all_rows{});  // row_ror 8
-      m = max_dpp(m, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});  // row_bcast 15
-      if (lrow == 31) s_amax[wn][wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3)] = m;
+      for (int c = 0; c < NC; ++c) {
+        const uint32_t v = __float_as_uint(acc[mi][c][i]) & 0x7fffffffu;
+        m = m > v ? m : v;
+      }
+      am[mi][i] = m;
     }
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0xB1>{}, all_rows{});
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0x4E>{}, all_rows{});
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0x124>{}, all_rows{});
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0x128>{}, all_rows{});
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});
+  if (lrow == 31) {
+    float* am_dst = &s_amax[wn][row0];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am_dst[drow(mi, i)] = __uint_as_float(am[mi][i]);
+  }
   __syncthreads();  // every wave is past its last ring read; s_amax complete
-  // E4M3 codes: lanes 4q..4q+3 hold 4 consecutive columns of a row; lane 4q gathers them
-  // (quad_perm broadcasts) and writes one dword of the [BM rows][128 B] code tile
+  // E4M3 codes: lanes 4q..4q+3 hold 4 consecutive columns of a row; each gathers all four
+  // (quad_perm broadcasts) and they write the same dword of the [BM rows][128 B] code tile.
+  // Every lane of a row computes the same UE8M0 byte and writes it to the [BM] array after
+  // the tile.  No lane masks, so the per-row work stays straight-line.
   uint8_t* stage_h = ring;
+  uint8_t* stage_sf = ring + BM * 128 + C::WN * BM * 4;
   auto from_lane = [](int v, auto ctrl) -> int {
     return __builtin_amdgcn_update_dpp(v, v, decltype(ctrl)::value, 0xf, 0xf, false);
   };
+  uint8_t* h_dst = stage_h + row0 * 128 + wn * (128 / C::WN) + (lrow & ~3);
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
-      const float amax = fmaxf(s_amax[0][r], s_amax[1][r]);
-      const int byte = ue8m0_for_amax(amax);
-      const float inv = inv_scale_of(byte);
+      const int r = row0 + drow(mi, i);
+      uint32_t mx = __float_as_uint(s_amax[0][r]);
+#pragma unroll
+      for (int w = 1; w < C::WN; ++w) {
+        const uint32_t o = __float_as_uint(s_amax[w][r]);
+        mx = mx > o ? mx : o;
+      }
+      const int sfb = ue8m0_for_amax(__uint_as_float(mx));
+      const float inv = inv_scale_of(sfb);
+      stage_sf[r] = (uint8_t)sfb;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int code = __builtin_amdgcn_cvt_pk_fp8_f32(acc[mi][c][i] * inv, 0.0f, 0, false) & 0xff;
-        const int word = code | (from_lane(code, std::integral_constant<int, 0x55>{}) << 8) |
+        const int word = from_lane(code, std::integral_constant<int, 0x00>{}) |
+                         (from_lane(code, std::integral_constant<int, 0x55>{}) << 8) |
                          (from_lane(code, std::integral_constant<int, 0xAA>{}) << 16) |
                          (from_lane(code, std::integral_constant<int, 0xFF>{}) << 24);
-        if ((lrow & 3) == 0) *reinterpret_cast<int*>(stage_h + r * 128 + wn * 64 + c * 32 + lrow) = word;
+        *reinterpret_cast<int*>(h_dst + drow(mi, i) * 128 + c * 32) = word;
       }
-      if (wn == 0 && lrow == 0 && r < rows) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = (uint8_t)byte;
     }
   __syncthreads();
   for (int q = tid; q < BM * 8; q += C::NTHR) {
     const int r = q >> 3, c = q & 7;
-    if (r < rows)
+    if (r < rows) {
       *reinterpret_cast<uint4*>(g.h + (long long)(row_begin + r) * g.I + n0 + c * 16) =
           *reinterpret_cast<const uint4*>(stage_h + r * 128 + c * 16);
+      if (c == 0) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = stage_sf[r];
+    }
   }
 }
 
-// plan[e] = number of m-tiles of experts before e; plan[EL] = all m-tiles
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int EL, int bm,
-                                                    int32_t* __restrict__ plan) {
-  __shared__ int a[2 * 1024 + 2];
-  for (int i = threadIdx.x; i < 2048; i += 1024) a[i] = 0;
-  __syncthreads();
-  for (int e = threadIdx.x; e < EL; e += 1024) a[e] = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-  __syncthreads();
-  block_exclusive_scan_2048(a);
-  for (int e = threadIdx.x; e <= EL; e += 1024) plan[e] = a[e];
-}
-
 // variant 0: 128-row tiles, 4 waves (FC1: 64-K stages x 3, FC2: 128 columns, 128-K stages
-//            x 2), small enough for two workgroups per CU: experts with few rows (decode).
+//            x 2), small enough for two workgroups per CU: experts with tens of rows.
 // variant 1: 256-row tiles (8 waves of 64x128, 128-K stages x 2): experts with many rows
 //            (prefill).  Measured on the prefill share against 64-K x 4 stages, 128x128 wave
 //            tiles and fragments read one stage ahead: this shape was fastest.
-int gemm_block_m(int variant) { return variant == 1 ? 256 : 128; }
+// variant 2: 32-row tiles, 4 waves side by side along the 256 weight rows, 128-K stages:
+//            experts with a handful of rows (decode), where the tile streams weights and
+//            the activation rows are a small part of each stage.
+int gemm_block_m(int variant) { return variant == 1 ? 256 : variant == 2 ? 32 : 128; }
 
 size_t gemm_max_mtiles(int rows_cap, int EL, int variant) {
   const int bm = gemm_block_m(variant);
@@ -589,12 +662,22 @@ bool gemm_supports(int H, int I) { return H / 128 <= kMaxKSteps && I / 128 <= kM
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
 static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
-  static_assert(NSTAGE * C::STAGE >= BM * 128 + 2 * BM * 4 && NSTAGE * C::STAGE >= BM * 4 + BM * 128,
+  static_assert(NSTAGE * C::STAGE >= BM * 128 + C::WN * BM * 4 + BM && NSTAGE * C::STAGE >= BM * 4 + BM * 128,
                 "the ring must hold the epilogue staging and the tile's token list");
   auto kern = grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   const size_t lds = (size_t)NSTAGE * C::STAGE + (size_t)BM * (a.K / 128) + 2 * (a.K / 128);
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // raise the kernel's dynamic LDS limit to its largest size (K = 8192) once per device
+  static std::atomic<uint64_t> ready{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(ready.load(std::memory_order_acquire) & bit)) {
+    const size_t most = (size_t)NSTAGE * C::STAGE + (size_t)(BM + 2) * kMaxKSteps;
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
+    if (e != hipSuccess) return e;
+    ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
   kern<<<dim3((unsigned)grid), dim3(NW * 64), lds, s>>>(a);
   return hipGetLastError();
 }
@@ -604,6 +687,10 @@ static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_
   if (variant == 1) {
     return wfmt == 0 ? launch_one<MODE, 0, 256, 256, 128, 2, 8, 64, 2>(a, grid, s)
                      : launch_one<MODE, 1, 256, 256, 128, 2, 8, 64, 2>(a, grid, s);
+  }
+  if (variant == 2) {
+    return wfmt == 0 ? launch_one<MODE, 0, 32, 256, 128, 2, 4, 32, 2>(a, grid, s)
+                     : launch_one<MODE, 1, 32, 256, 128, 3, 4, 32, 2>(a, grid, s);
   }
   // small experts: two workgroups fit one CU (<= 80 KB of LDS each) so one streams weights
   // while the other is in its prologue or epilogue; FC2 tiles are 128 columns wide
@@ -617,14 +704,9 @@ static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_
 hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
                       const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
                       uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s) {
-  if (!plan_ready) {
-    plan_kernel<<<1, 1024, 0, s>>>(offsets, sh.EL, gemm_block_m(variant), plan);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   GemmArgs a{};
   a.A = x; a.A_sf = x_sf; a.row_to_slot = row_to_slot; a.B = w1; a.B_sf = w1_sf;
-  a.offsets = offsets; a.plan = plan; a.h = h; a.h_sf = h_sf;
+  a.offsets = offsets; a.plan = plan_ready ? plan : nullptr; a.h = h; a.h_sf = h_sf;
   a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.n_tiles = sh.I / 128;
   a.b_estride = sh.wfmt == 0 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
   a.bsf_estride = sh.wfmt == 0 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
@@ -638,17 +720,13 @@ hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint
 hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
                       const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, bool plan_ready,
                       hipStream_t s) {
-  if (!plan_ready) {
-    plan_kernel<<<1, 1024, 0, s>>>(offsets, sh.EL, gemm_block_m(variant), plan);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   GemmArgs a{};
-  a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets; a.plan = plan; a.y2 = y2;
+  a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets; a.plan = plan_ready ? plan : nullptr;
+  a.y2 = y2;
   a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL;
   a.b_estride = sh.wfmt == 0 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt == 0 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
-  const int bn = variant == 1 ? 256 : 128;
+  const int bn = variant == 0 ? 128 : 256;
   a.n_tiles = (sh.H + bn - 1) / bn;
   const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
   if (grid == 0) return hipSuccess;

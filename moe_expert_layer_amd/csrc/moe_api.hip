@@ -47,7 +47,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace regions (byte offsets from the workspace base).
 struct Layout {
-  size_t ids, w, counts, offsets, r2s, s2r, chunk_cnt, chunk_base, plan1, plan2, h, h_sf, y2, total;
+  size_t ids, w, counts, offsets, r2s, s2r, chunk_cnt, chunk_base, plan1, h, h_sf, y2, total;
 };
 
 Layout make_layout(const moe_layer_desc& d) {
@@ -70,7 +70,6 @@ Layout make_layout(const moe_layer_desc& d) {
   L.chunk_cnt = take(nchunks * NB * 4);
   L.chunk_base = take(nchunks * NB * 4);
   L.plan1 = take(NB * 4);
-  L.plan2 = take(NB * 4);
   L.h = take(cap * (size_t)d.inter);
   L.h_sf = take(cap * (size_t)(d.inter / 128));
   L.y2 = take(cap * (size_t)d.hidden * 4);
@@ -104,7 +103,7 @@ moe_status check_desc(const moe_layer_desc* d) {
     if (!std::isfinite(d->act_alpha) || !std::isfinite(d->act_up_bias))
       return fail(MOE_ERR_INVALID_DESC, "act_alpha / act_up_bias must be finite");
   }
-  if (d->variant < -1 || d->variant > 1) return fail(MOE_ERR_INVALID_DESC, "variant %d unknown", d->variant);
+  if (d->variant < -1 || d->variant > 2) return fail(MOE_ERR_INVALID_DESC, "variant %d unknown", d->variant);
   if (!moe::gemm_supports(d->hidden, d->inter))
     return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d above the supported 8192", d->hidden, d->inter);
   if ((long long)d->num_tokens * d->hidden >= (1LL << 32))
@@ -161,8 +160,12 @@ moe::Shape shape_of(const moe_layer_desc& d) {
 // Chosen from the descriptor only, so no host synchronisation is needed.
 int pick_variant(const moe_layer_desc& d) {
   if (d.variant >= 0) return d.variant;
+  // the routing is on the device: the bound T * min(k, E_loc) on the local rows stands in
+  // for their count; tiles are sized for its average per local expert
   const long long most_rows = (long long)d.num_tokens * (d.topk < d.num_local ? d.topk : d.num_local);
-  return most_rows >= 256LL * d.num_local ? 1 : 0;
+  if (most_rows >= 256LL * d.num_local) return 1;
+  if (most_rows <= 48LL * d.num_local) return 2;
+  return 0;
 }
 
 #define MOE_TRY_HIP(call)                                                            \
@@ -254,7 +257,7 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* d, const uint8_t* x, con
   const Layout L = make_layout(*d);
   const moe::Shape sh = shape_of(*d);
   MOE_TRY_HIP(moe::launch_fc1(sh, pick_variant(*d), x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
-                              region<int32_t>(ws, L.plan1), false, (hipStream_t)stream));
+                              nullptr, false, (hipStream_t)stream));
   return ok();
 }
 
@@ -273,7 +276,7 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* d, const uint8_t* h, co
   const Layout L = make_layout(*d);
   const moe::Shape sh = shape_of(*d);
   float* y2 = region<float>(ws, L.y2);
-  MOE_TRY_HIP(moe::launch_fc2(sh, pick_variant(*d), h, h_sf, w2, w2_sf, offsets, y2, region<int32_t>(ws, L.plan2),
+  MOE_TRY_HIP(moe::launch_fc2(sh, pick_variant(*d), h, h_sf, w2, w2_sf, offsets, y2, nullptr,
                               false, (hipStream_t)stream));
   MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, y, (hipStream_t)stream));
   return ok();

@@ -33,8 +33,9 @@ int gemm_block_m(int variant);
 // largest contraction the GEMM kernels stage scales for (K / 128 <= 64)
 bool gemm_supports(int H, int I);
 size_t gemm_max_mtiles(int rows_cap, int EL, int variant);
-// plan_ready: `plan` already holds the tile plan of these offsets for this variant's tile rows
-// (written by launch_permute); otherwise it is computed first.
+// plan_ready: `plan` holds the tile plan of these offsets for this variant's tile rows (written
+// by launch_permute); otherwise `plan` is ignored and every GEMM workgroup derives the plan
+// from `offsets` in its prologue.
 hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
                       const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
                       uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s);

@@ -73,8 +73,8 @@ def test_layer_parity_small(name, w):
     assert np.all(fused["y_bf16"][nol] == 0)
 
 
-@pytest.mark.parametrize("variant", [0, 1])
-@pytest.mark.parametrize("name", ["ragged_oai", "zipf_small", "mxfp4_small", "k16_e1024"])
+@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("name", ["ragged_oai", "ragged_h384_share", "zipf_small", "mxfp4_small", "k16_e1024"])
 def test_layer_parity_forced_variant(name, variant):
     w = dict(_small_cases())[name]
     G.say(f"[variant] {name} variant={variant}")
@@ -97,7 +97,8 @@ def test_run_twice_bit_identical():
     assert np.array_equal(a["y_bf16"], b["y_bf16"])
 
 
-def test_exact_integer_layer_bit_exact():
+@pytest.mark.parametrize("variant", [-1, 0, 1, 2])
+def test_exact_integer_layer_bit_exact(variant):
     """Small-integer operands, unit scales, top-1, OAI with alpha 0: every partial sum is exact in
     fp32 (x, W2 in {-1, 0, 1}; W1 rows with at most 4 non-zeros so |g|, |u| <= 4 and h = g*u/2 is a
     half-integer <= 8 that the requant reproduces exactly), so the GPU output equals the oracle bit for bit."""
@@ -121,7 +122,7 @@ def test_exact_integer_layer_bit_exact():
            "w1_sf": np.full((E, 2 * I // 128, H // 128), 127, np.uint8), "w2": pm1((E, H, I), 0.3),
            "w2_sf": np.full((E, H // 128, I // 128), 127, np.uint8)}
     ref = O.layer(w, inp)
-    got = G.run_split(w, G.upload(inp))
+    got = G.run_split(w, G.upload(inp), variant=variant)
     assert np.array_equal(got["h"], ref["h"]) and np.array_equal(got["h_sf"], ref["h_sf"])
     assert np.array_equal(got["y_bf16"], ref["y_bf16"])
 
