@@ -22,6 +22,10 @@
 // K bytes [16kb, +16) and [32 + 16kb, +16); an FP4 operand holds K elements [32kb, +32)
 // (element 2i in the low nibble of byte i); lane l's scale byte covers row/column l%32
 // and the 32-wide K block kb; result lane l holds rows 8*(i/4) + 4*(l/32) + i%4, column l%32.
+// FC1 feeds the weights as the first operand and the tokens as the second, so a lane's
+// results are one token row and runs of 4 consecutive h columns (the epilogue's amax and
+// E4M3 packing then stay mostly inside the lane); FC2 keeps tokens first (row-contiguous
+// Y2 stores).
 //
 // Tiles: 128 rows x BN weight rows (FC1: BN = 256 = 128 gate + the matching 128 up rows,
 // i.e. exactly one 1x128 requant block of h; FC2: BN output columns), 4 waves in 2x2.
@@ -413,9 +417,13 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
       for (int ct = 0; ct < C::NT; ++ct)
 #pragma unroll
         for (int mi = 0; mi < NL; ++mi)
-          acc[mi][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[h][mi], f.b[h][ct], acc[mi][ct], 0,
-                                                                        WFMT == 0 ? 0 : 4, 0, f.sa[mi], 0,
-                                                                        f.sb[h][ct]);
+          acc[mi][ct] = MODE == 1
+                            ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[h][ct], f.a[h][mi], acc[mi][ct],
+                                                                              WFMT == 0 ? 0 : 4, 0, 0, f.sb[h][ct],
+                                                                              0, f.sa[mi])
+                            : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[h][mi], f.b[h][ct], acc[mi][ct], 0,
+                                                                              WFMT == 0 ? 0 : 4, 0, f.sa[mi], 0,
+                                                                              f.sb[h][ct]);
   };
   const int live_tiles = min(C::MI, max(0, (rows - wm * WTM + 31) / 32));
   auto mma = [&](const auto& f) {
@@ -492,8 +500,10 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   }
 
   if (MODE == 2) {
-    // ---- FC2 epilogue: fp32 rows of Y2 (32 consecutive columns per lane group), stored
-    //      non-temporally so the burst at the end of the tiles does not evict the operands ----
+    // ---- FC2 epilogue (tokens are the MFMA's first operand: lane l of acc[mi][ct] holds
+    //      rows 8*(i/4) + 4*kb + i%4 of row tile mi, column bcol(ct) + l%32): fp32 rows of Y2,
+    //      32 consecutive columns per lane group, stored non-temporally so the burst at the
+    //      end of the tiles does not evict the operands ----
     if (wave_live) {
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi)
@@ -513,14 +523,15 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
     return;
   }
 
+  // FC1 accumulator layout (weights are the MFMA's first operand, tokens its second, so a
+  // lane holds one tile row): lane l of acc[mi][ct] holds tile row wm*WTM + mi*32 + l%32 and,
+  // for value i, weight row bcol(ct) + 8*(i/4) + 4*kb + i%4, i.e. runs of 4 consecutive
+  // columns.
+  const int trow = wm * WTM + lrow;  // tile row of row tile 0 of this lane
   // ---- FC1 epilogue: activation, 1x128 amax, UE8M0 scale, E4M3 codes ----
-  // lane holds rows 8*(i/4) + 4*kb + i%4 of each row tile; h column wn*128/WN + c*32 + lrow.
-  // Each step runs over all of the lane's values as straight-line code, with the LDS writes
-  // of a step gathered under one lane mask, so independent chains interleave.
+  // The lane's values of row tile mi all belong to tile row trow + mi*32: gate in
+  // acc[mi][c], up in acc[mi][c + NC] at h column wn*128/WN + c*32 + 8*(i/4) + 4*kb + i%4.
   constexpr int NC = C::NT / 2;
-  // row of value i of row tile mi relative to the lane's first row (a compile-time constant)
-  auto drow = [](int mi, int i) { return mi * 32 + 8 * (i >> 2) + (i & 3); };
-  const int row0 = wm * WTM + 4 * kb;
   if (g.act == 1) {
     const float cl = g.clamp, al = g.alpha, bi = g.bias;
 #pragma unroll
@@ -544,98 +555,58 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
           acc[mi][c][i] = gt * sigmoidf_(gt) * acc[mi][c + NC][i];
         }
   }
-  // amax of each tile row over the wave's columns, as an unsigned max of the (non-negative)
-  // float bits: a DPP max within each 16-lane row (quad swaps, then rotations by 4 and 8),
-  // then row 1 (3) takes row 0's (2's) result through row_bcast:15, so lanes 16-31 and 48-63
-  // hold the maximum over their 32-lane half
-  auto max_dpp = [](uint32_t m, auto ctrl, auto row_mask) -> uint32_t {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, decltype(ctrl)::value,
-                                                             decltype(row_mask)::value, 0xf, false);
-    return m > o ? m : o;
-  };
-  using all_rows = std::integral_constant<int, 0xf>;
-  uint32_t am[C::MI][16];
+  // amax of each row: over the lane's values (an unsigned max of the non-negative float
+  // bits), then with lane l ^ 32 (the other half of the columns), then across the WN waves
+  // through LDS.  Both lanes of a pair write the same value to the same place.
 #pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi) {
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t m = 0;
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+      for (int i = 0; i < 16; ++i) {
         const uint32_t v = __float_as_uint(acc[mi][c][i]) & 0x7fffffffu;
         m = m > v ? m : v;
       }
-      am[mi][i] = m;
-    }
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0xB1>{}, all_rows{});
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0x4E>{}, all_rows{});
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0x124>{}, all_rows{});
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0x128>{}, all_rows{});
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      am[mi][i] = max_dpp(am[mi][i], std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});
-  if (lrow == 31) {
-    float* am_dst = &s_amax[wn][row0];
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) am_dst[drow(mi, i)] = __uint_as_float(am[mi][i]);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)m);
+    s_amax[wn][trow + mi * 32] = __uint_as_float(m > o ? m : o);
   }
   __syncthreads();  // every wave is past its last ring read; s_amax complete
-  // E4M3 codes: lanes 4q..4q+3 hold 4 consecutive columns of a row; each gathers all four
-  // (quad_perm broadcasts) and they write the same dword of the [BM rows][128 B] code tile.
-  // Every lane of a row computes the same UE8M0 byte and writes it to the [BM] array after
-  // the tile.  No lane masks, so the per-row work stays straight-line.
+  // E4M3 codes, four consecutive columns per dword (two packed conversions), into the
+  // [BM rows][128 B] code tile with its 16-byte chunks XOR-swizzled by row (the rows of one
+  // wave's writes then spread over the banks); the UE8M0 byte of each row goes to a [BM]
+  // array after it.  Every lane of a row computes the same byte.
   uint8_t* stage_h = ring;
   uint8_t* stage_sf = ring + BM * 128 + C::WN * BM * 4;
-  auto from_lane = [](int v, auto ctrl) -> int {
-    return __builtin_amdgcn_update_dpp(v, v, decltype(ctrl)::value, 0xf, 0xf, false);
-  };
-  uint8_t* h_dst = stage_h + row0 * 128 + wn * (128 / C::WN) + (lrow & ~3);
 #pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi) {
+    const int r = trow + mi * 32;
+    uint32_t mx = __float_as_uint(s_amax[0][r]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = row0 + drow(mi, i);
-      uint32_t mx = __float_as_uint(s_amax[0][r]);
-#pragma unroll
-      for (int w = 1; w < C::WN; ++w) {
-        const uint32_t o = __float_as_uint(s_amax[w][r]);
-        mx = mx > o ? mx : o;
-      }
-      const int sfb = ue8m0_for_amax(__uint_as_float(mx));
-      const float inv = inv_scale_of(sfb);
-      stage_sf[r] = (uint8_t)sfb;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(acc[mi][c][i] * inv, 0.0f, 0, false) & 0xff;
-        const int word = from_lane(code, std::integral_constant<int, 0x00>{}) |
-                         (from_lane(code, std::integral_constant<int, 0x55>{}) << 8) |
-                         (from_lane(code, std::integral_constant<int, 0xAA>{}) << 16) |
-                         (from_lane(code, std::integral_constant<int, 0xFF>{}) << 24);
-        *reinterpret_cast<int*>(h_dst + drow(mi, i) * 128 + c * 32) = word;
-      }
+    for (int w = 1; w < C::WN; ++w) {
+      const uint32_t o = __float_as_uint(s_amax[w][r]);
+      mx = mx > o ? mx : o;
     }
+    const int sfb = ue8m0_for_amax(__uint_as_float(mx));
+    const float inv = inv_scale_of(sfb);
+    stage_sf[r] = (uint8_t)sfb;
+    uint8_t* hrow = stage_h + r * 128;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(acc[mi][c][4 * q] * inv, acc[mi][c][4 * q + 1] * inv, 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(acc[mi][c][4 * q + 2] * inv, acc[mi][c][4 * q + 3] * inv, word, true);
+        const int col = wn * (128 / C::WN) + c * 32 + 8 * q + 4 * kb;  // multiple of 4
+        *reinterpret_cast<int*>(hrow + ((((col >> 4) ^ (r & 7)) << 4) | (col & 15))) = word;
+      }
+  }
   __syncthreads();
   for (int q = tid; q < BM * 8; q += C::NTHR) {
     const int r = q >> 3, c = q & 7;
     if (r < rows) {
       *reinterpret_cast<uint4*>(g.h + (long long)(row_begin + r) * g.I + n0 + c * 16) =
-          *reinterpret_cast<const uint4*>(stage_h + r * 128 + c * 16);
+          *reinterpret_cast<const uint4*>(stage_h + r * 128 + ((c ^ (r & 7)) << 4));
       if (c == 0) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = stage_sf[r];
     }
   }
