@@ -197,6 +197,25 @@ def main():
             traffic = tj.get("bytes_per_launch")
     roof["traffic"] = traffic
 
+    # input quantisation (bf16 -> E4M3 + 1x128 UE8M0) of this workload's activations, HBM-bound
+    xb = torch.randn((T, w.hidden), device="cuda").to(torch.bfloat16)
+    xq = torch.empty((T, w.hidden), dtype=torch.uint8, device="cuda")
+    xq_sf = torch.empty((T, w.hidden // 128), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        B.moe_quantize_act(d, xb, xq, xq_sf, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.kernel_steps):
+        B.moe_quantize_act(d, xb, xq, xq_sf, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    q_ms = e0.elapsed_time(e1) / args.kernel_steps
+    q_bytes = T * w.hidden * (2 + 1 + 1 / 128)
+    input_quant = {"kernel": "quantize_act_kernel (moe_quantize_act)", "kernel_ms": round(q_ms, 4),
+                   "bytes": int(q_bytes), "achieved": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                   "peak": PEAK_HBM_GBS, "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del xb, xq, xq_sf
+
     tflops = alg["flops"] / (ms * 1e-3) / 1e12
     out = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -212,6 +231,7 @@ def main():
         "pct_hbm_peak": round(100 * alg["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "wall_ms_timed_region": round(wall_ms, 2),
         "roofline": roof,
+        "input_quant": input_quant,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)

@@ -155,6 +155,18 @@ moe_status moe_layer(const moe_layer_desc* desc, const float* logits, const uint
                      int32_t* opt_slot_to_row, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Input quantisation (the pages' "DSV4 o_proj: fuse fp8/UE8M0 quantize into o_a proj",
+ * Description: FP8 E4M3 with one UE8M0 scale per 1x128 block, from an amax per block).
+ * x_bf16 [T, H] bf16 bits -> x [T, H] E4M3 codes and x_sf [T, H/128] UE8M0 bytes, the
+ * layout moe_layer and moe_grouped_fc1_swiglu read.  The rule is the one used for the
+ * intermediate h: scale 2^e with the smallest e such that 448 * 2^e >= amax of the block
+ * (byte e + 127 clamped to [0, 254]; 127 for an all-zero block), codes E4M3
+ * round-to-nearest-even of v * 2^-e.  Deterministic and exact for finite inputs.
+ * Uses desc->num_tokens and desc->hidden; x_bf16 and x must be 16-byte aligned. No
+ * workspace; asynchronous on `stream`. */
+moe_status moe_quantize_act(const moe_layer_desc* desc, const uint16_t* x_bf16, uint8_t* x, uint8_t* x_sf,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,8 @@ def lib():
         L.moe_grouped_fc2_combine.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, VP]
         L.moe_layer.restype = I32
         L.moe_layer.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, VP]
+        L.moe_quantize_act.restype = I32
+        L.moe_quantize_act.argtypes = [D, P, P, P, VP]
         _lib = L
     return _lib
 
@@ -147,6 +149,11 @@ def moe_layer(desc, logits, x, x_sf, w1, w1_sf, w2, w2_sf, y, workspace, topk_id
                            _ptr(w2_sf), _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
                            _ptr(row_to_slot), _ptr(slot_to_row), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_quantize_act(desc, x_bf16, x, x_sf, stream=None):
+    """bf16 activations [T, H] (int16/uint16/bfloat16 tensor) -> E4M3 codes x [T, H] and UE8M0 x_sf [T, H/128]."""
+    _check(lib().moe_quantize_act(ctypes.byref(desc), _ptr(x_bf16), _ptr(x), _ptr(x_sf), _stream(stream)))
 
 
 def alloc_workspace(desc, device="cuda"):

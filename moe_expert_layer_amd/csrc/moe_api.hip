@@ -316,4 +316,15 @@ moe_status moe_layer(const moe_layer_desc* d, const float* logits, const uint8_t
   return ok();
 }
 
+moe_status moe_quantize_act(const moe_layer_desc* d, const uint16_t* x_bf16, uint8_t* x, uint8_t* x_sf,
+                            void* stream) {
+  if (moe_status st = check_desc(d)) return st;
+  if (d->num_tokens == 0) return ok();
+  if (!x_bf16 || !x || !x_sf) return fail(MOE_ERR_NULL, "x_bf16/x/x_sf NULL");
+  if (misaligned(x_bf16, 16) || misaligned(x, 16)) return fail(MOE_ERR_MISALIGNED, "x_bf16/x not 16-byte aligned");
+  if (moe_status st = check_device()) return st;
+  MOE_TRY_HIP(moe::launch_quantize_act(x_bf16, (long long)d->num_tokens * d->hidden, x, x_sf, (hipStream_t)stream));
+  return ok();
+}
+
 }  // extern "C"

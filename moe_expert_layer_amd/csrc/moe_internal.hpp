@@ -43,6 +43,10 @@ hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint
                       const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, bool plan_ready,
                       hipStream_t s);
 
+// input quantisation --------------------------------------------------------
+// n = T * H bf16 values (H % 128 == 0) -> E4M3 codes [n] and UE8M0 bytes [n / 128]
+hipError_t launch_quantize_act(const uint16_t* x_bf16, long long n, uint8_t* x, uint8_t* x_sf, hipStream_t s);
+
 // combine --------------------------------------------------------------------
 hipError_t launch_combine(const float* y2, const int32_t* slot_to_row, const float* topk_w, int T, int H, int k,
                           uint16_t* y, hipStream_t s);

@@ -149,8 +149,11 @@ def _bf16_round(v: np.ndarray) -> np.ndarray:
     return torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
 
 
-def generate(w: Workload, seed: int | None = None, threads: int = 8) -> Dict[str, np.ndarray]:
+def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: bool = False) -> Dict[str, np.ndarray]:
     """All layer inputs for workload ``w`` as host numpy arrays (seeded, deterministic).
+
+    ``with_bf16`` also returns the bf16 activations before their quantisation, as bit
+    patterns ``x_bf16`` [T, H] uint16.
 
     Seed tree: SeedSequence(seed).spawn(2 + 2 * E_loc) gives the streams for the logits,
     the activations, then W1 and W2 of each local expert in order; experts are drawn in
@@ -166,8 +169,10 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8) -> Dict[str
         logits = (logits + prior[None, :]).astype(np.float32)
     xf = _bf16_round(rng(1).standard_normal((T, H), dtype=np.float32))
     x, x_sf = _quant_fp8_blocks(xf, 1, 128)
-    del xf
     out = {"logits": np.ascontiguousarray(logits), "x": x, "x_sf": x_sf}
+    if with_bf16:
+        out["x_bf16"] = (xf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    del xf
     fp8 = w.weight_format == "fp8"
     w1 = np.empty((EL, 2 * I, H if fp8 else H // 2), np.uint8)
     w1_sf = np.empty((EL, 2 * I // 128, H // 128) if fp8 else (EL, 2 * I, H // 32), np.uint8)

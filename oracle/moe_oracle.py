@@ -14,6 +14,7 @@ one GPU's share of the experts, written from the pages' description of the fused
              against FP8 E4M3 weights with 128x128 UE8M0 block scales (or MXFP4)
   activation SwiGLU, or parameterised OAI-SwiGLU (clamp, sigmoid alpha, up bias)
   requant    the intermediate back to FP8 E4M3 with one UE8M0 scale per 1x128 block
+  quantize   (input side) bf16 activations to FP8 E4M3 with the same 1x128 UE8M0 rule
   FC2        down projection of the requantised intermediate
   combine    top-k weighted sum of each token's local rows, back in token order
 
@@ -241,6 +242,23 @@ def requant_1x128(h32: np.ndarray):
     scaled = blk * np.ldexp(1.0, -(byte - 127))[:, :, None]
     codes = encode_e4m3_rne(scaled).reshape(n, i)
     return codes, byte.astype(np.uint8)
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 (the upper half of the float32 pattern; exact)."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def quantize_act(x_bf16_bits: np.ndarray):
+    """Input quantisation: bf16 rows [T, H] -> E4M3 codes [T, H] and UE8M0 bytes [T, H/128].
+
+    The activations' FP8 E4M3 format with one UE8M0 scale per 128 consecutive values
+    ("DSV4 o_proj: fuse fp8/UE8M0 quantize into o_a proj", Description) under the same
+    scale rule as the intermediate: bf16 values are exact in float32, so this is
+    ``requant_1x128`` of the decoded rows.
+    """
+    return requant_1x128(decode_bf16(x_bf16_bits))
 
 
 def expert_rows(d, inputs, e: int, tokens: np.ndarray):

@@ -121,3 +121,12 @@ def test_oversized_activation_matrix_unsupported(L):
     assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED
     d.num_tokens = (1 << 32) // d.hidden - 1
     assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_OK
+
+
+def test_quantize_act_validation(L):
+    d = B.desc_from_workload(synth.workload("tiny"))
+    P = ctypes.c_void_p
+    assert L.moe_quantize_act(ctypes.byref(d), None, None, None, None) == B.MOE_ERR_NULL
+    assert L.moe_quantize_act(ctypes.byref(d), P(0x1008), P(0x2000), P(0x3000), None) == B.MOE_ERR_MISALIGNED
+    d.hidden = 100
+    assert L.moe_quantize_act(ctypes.byref(d), P(0x1000), P(0x2000), P(0x3000), None) == B.MOE_ERR_INVALID_DESC

@@ -1,0 +1,71 @@
+"""GPU parity of the input quantisation (moe_quantize_act) against the oracle, bit for bit.
+
+bf16 values are exact in fp32 and the scaling is by a power of two, so codes and scale
+bytes are fully determined: the bar is equality of every byte.
+"""
+import numpy as np
+import pytest
+
+from moe_expert_layer_amd import synth
+from oracle import moe_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from moe_expert_layer_amd import binding as B
+    from tests import gpu_util as G
+
+
+def _bits(v32):
+    return (np.asarray(v32, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _run(bits):
+    T, H = bits.shape
+    d = B.make_desc(num_tokens=T, hidden=H, inter=128, num_experts=1, topk=1)
+    xb = torch.from_numpy(bits.view(np.int16)).cuda()
+    x = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((T, H // 128), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_act(d, xb, x, sf)
+    torch.cuda.synchronize()
+    return x.cpu().numpy(), sf.cpu().numpy()
+
+
+def _cases():
+    rng = np.random.default_rng(40)
+    n = lambda *s: rng.standard_normal(s).astype(np.float32)
+    special = np.concatenate([np.zeros((1, 256)), -np.zeros((1, 256)), n(1, 256) * 1e-38, n(1, 256) * 8e37,
+                              np.concatenate([np.zeros((1, 128)), n(1, 128)], 1)]).astype(np.float32)
+    return [("n01_1x128", n(1, 128)), ("n01_37x384", n(37, 384)), ("n01_300x2048", n(300, 2048)),
+            ("cauchy_129x7168", rng.standard_cauchy((129, 7168)).astype(np.float32)),
+            ("tiny_8x1024", n(8, 1024) * 1e-30), ("large_8x1024", n(8, 1024) * 1e30), ("special", special)]
+
+
+@pytest.mark.parametrize("name,v", _cases(), ids=[c[0] for c in _cases()])
+def test_quantize_bit_exact(name, v):
+    bits = _bits(synth._bf16_round(np.asarray(v, np.float32)))
+    G.say(f"[quant] {name}: {bits.shape}")
+    q, sf = _run(bits)
+    rq, rsf = O.quantize_act(bits)
+    assert np.array_equal(sf, rsf)
+    assert np.array_equal(q, rq)
+
+
+def test_quantize_zero_tokens_is_a_noop():
+    d = B.make_desc(num_tokens=0, hidden=256, inter=128, num_experts=1, topk=1)
+    B.moe_quantize_act(d, None, None, None)
+
+
+@pytest.mark.parametrize("cfg", ["decode", "mxfp4_large"])
+def test_quantize_fullsize(cfg):
+    """Full-size activations: every byte against the seeded inputs (which the CPU tests pin to
+    the oracle), and 16 sampled rows against the oracle directly."""
+    w = synth.workload(cfg)
+    inp = synth.generate(w, with_bf16=True)
+    G.say(f"[quant] fullsize {cfg}: T={w.tokens} H={w.hidden}")
+    q, sf = _run(inp["x_bf16"])
+    assert np.array_equal(sf, inp["x_sf"]) and np.array_equal(q, inp["x"])
+    rows = np.random.default_rng(41).choice(w.tokens, size=min(16, w.tokens), replace=False)
+    rq, rsf = O.quantize_act(inp["x_bf16"][rows])
+    assert np.array_equal(q[rows], rq) and np.array_equal(sf[rows], rsf)
