@@ -167,6 +167,19 @@ moe_status moe_layer(const moe_layer_desc* desc, const float* logits, const uint
 moe_status moe_quantize_act(const moe_layer_desc* desc, const uint16_t* x_bf16, uint8_t* x, uint8_t* x_sf,
                             void* stream);
 
+/* Packed UE8M0 scale interop (the pages' "DSV4 o_proj: fuse fp8/UE8M0 quantize into o_a
+ * proj": the FP8-output tactic's int32 scale tensor of shape (M, ceil(G/4)) with MN-major
+ * stride (1, aligned_M), aligned_M = M rounded up to 4, padding zeroed).
+ * moe_pack_scales: sf [rows, groups] UE8M0 bytes (the layout of x_sf and h_sf) -> packed,
+ * an int32 buffer of ceil(groups/4) * aligned_rows words where word (m, j) is at
+ * j * aligned_rows + m and holds groups 4j..4j+3 of row m, group 4j+b in byte b
+ * (little-endian); every padding row and byte is written as zero.
+ * moe_unpack_scales: the inverse (padding is not read).
+ * rows >= 0, 1 <= groups, rows * groups < 2^31; packed must be 4-byte aligned.
+ * Asynchronous on `stream`. */
+moe_status moe_pack_scales(int32_t rows, int32_t groups, const uint8_t* sf, int32_t* packed, void* stream);
+moe_status moe_unpack_scales(int32_t rows, int32_t groups, const int32_t* packed, uint8_t* sf, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,10 @@ def lib():
         L.moe_layer.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, VP]
         L.moe_quantize_act.restype = I32
         L.moe_quantize_act.argtypes = [D, P, P, P, VP]
+        L.moe_pack_scales.restype = I32
+        L.moe_pack_scales.argtypes = [I32, I32, P, P, VP]
+        L.moe_unpack_scales.restype = I32
+        L.moe_unpack_scales.argtypes = [I32, I32, P, P, VP]
         _lib = L
     return _lib
 
@@ -154,6 +158,16 @@ def moe_layer(desc, logits, x, x_sf, w1, w1_sf, w2, w2_sf, y, workspace, topk_id
 def moe_quantize_act(desc, x_bf16, x, x_sf, stream=None):
     """bf16 activations [T, H] (int16/uint16/bfloat16 tensor) -> E4M3 codes x [T, H] and UE8M0 x_sf [T, H/128]."""
     _check(lib().moe_quantize_act(ctypes.byref(desc), _ptr(x_bf16), _ptr(x), _ptr(x_sf), _stream(stream)))
+
+
+def moe_pack_scales(rows, groups, sf, packed, stream=None):
+    """UE8M0 bytes [rows, groups] -> packed int32 words [ceil(groups/4) * pad_up(rows, 4)] (MN-major)."""
+    _check(lib().moe_pack_scales(rows, groups, _ptr(sf), _ptr(packed), _stream(stream)))
+
+
+def moe_unpack_scales(rows, groups, packed, sf, stream=None):
+    """Inverse of moe_pack_scales."""
+    _check(lib().moe_unpack_scales(rows, groups, _ptr(packed), _ptr(sf), _stream(stream)))
 
 
 def alloc_workspace(desc, device="cuda"):

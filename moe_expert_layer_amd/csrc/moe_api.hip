@@ -327,4 +327,30 @@ moe_status moe_quantize_act(const moe_layer_desc* d, const uint16_t* x_bf16, uin
   return ok();
 }
 
+namespace {
+moe_status check_pack_args(int32_t rows, int32_t groups, const void* a, const void* b, const void* packed) {
+  if (rows < 0 || groups < 1 || (long long)rows * groups >= (1LL << 31))
+    return fail(MOE_ERR_INVALID_DESC, "rows %d / groups %d out of range", rows, groups);
+  if (rows > 0 && (!a || !b)) return fail(MOE_ERR_NULL, "sf/packed NULL");
+  if (misaligned(packed, 4)) return fail(MOE_ERR_MISALIGNED, "packed not 4-byte aligned");
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_pack_scales(int32_t rows, int32_t groups, const uint8_t* sf, int32_t* packed, void* stream) {
+  if (moe_status st = check_pack_args(rows, groups, sf, packed, packed)) return st;
+  if (rows == 0) return ok();
+  if (moe_status st = check_device()) return st;
+  MOE_TRY_HIP(moe::launch_pack_scales(sf, rows, groups, packed, (hipStream_t)stream));
+  return ok();
+}
+
+moe_status moe_unpack_scales(int32_t rows, int32_t groups, const int32_t* packed, uint8_t* sf, void* stream) {
+  if (moe_status st = check_pack_args(rows, groups, packed, sf, packed)) return st;
+  if (rows == 0) return ok();
+  if (moe_status st = check_device()) return st;
+  MOE_TRY_HIP(moe::launch_unpack_scales(packed, rows, groups, sf, (hipStream_t)stream));
+  return ok();
+}
+
 }  // extern "C"

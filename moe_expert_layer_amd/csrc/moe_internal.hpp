@@ -46,6 +46,9 @@ hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint
 // input quantisation --------------------------------------------------------
 // n = T * H bf16 values (H % 128 == 0) -> E4M3 codes [n] and UE8M0 bytes [n / 128]
 hipError_t launch_quantize_act(const uint16_t* x_bf16, long long n, uint8_t* x, uint8_t* x_sf, hipStream_t s);
+// UE8M0 bytes [M, G] <-> packed int32 [ceil(G/4)][pad_up(M, 4)] (MN-major, padding zeroed)
+hipError_t launch_pack_scales(const uint8_t* sf, int M, int G, int32_t* packed, hipStream_t s);
+hipError_t launch_unpack_scales(const int32_t* packed, int M, int G, uint8_t* sf, hipStream_t s);
 
 // combine --------------------------------------------------------------------
 hipError_t launch_combine(const float* y2, const int32_t* slot_to_row, const float* topk_w, int T, int H, int k,

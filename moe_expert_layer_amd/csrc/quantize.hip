@@ -66,4 +66,53 @@ hipError_t launch_quantize_act(const uint16_t* x_bf16, long long n, uint8_t* x, 
   return hipGetLastError();
 }
 
+// Packed UE8M0 scales ("DSV4 o_proj: fuse fp8/UE8M0 quantize into o_a proj": the o_a
+// FP8-output tactic checks an int32 scale tensor of shape (M, ceil(G/4)) with MN-major
+// stride (1, aligned_M), aligned_M = M rounded up to 4, padding zeroed).  Word (m, j) sits at
+// j * aligned_M + m and holds groups 4j .. 4j+3 of row m, group 4j + b in byte b.
+// One thread per word: consecutive threads write consecutive words.
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ sf, int M, int G, int AM,
+                                                          long long nwords, uint32_t* __restrict__ packed) {
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (q >= nwords) return;
+  const int j = (int)(q / AM), m = (int)(q - (long long)j * AM);
+  uint32_t w = 0;
+  if (m < M) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (4 * j + b < G) w |= (uint32_t)sf[(long long)m * G + 4 * j + b] << (8 * b);
+  }
+  packed[q] = w;
+}
+
+__global__ __launch_bounds__(256) void unpack_scales_kernel(const uint32_t* __restrict__ packed, int M, int G, int AM,
+                                                            long long nwords, uint8_t* __restrict__ sf) {
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (q >= nwords) return;
+  const int j = (int)(q / AM), m = (int)(q - (long long)j * AM);
+  if (m >= M) return;
+  const uint32_t w = packed[q];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    if (4 * j + b < G) sf[(long long)m * G + 4 * j + b] = (uint8_t)(w >> (8 * b));
+}
+
+hipError_t launch_pack_scales(const uint8_t* sf, int M, int G, int32_t* packed, hipStream_t s) {
+  const int AM = (M + 3) / 4 * 4;
+  const long long nwords = (long long)((G + 3) / 4) * AM;
+  if (nwords == 0) return hipSuccess;
+  pack_scales_kernel<<<dim3((unsigned)((nwords + 255) / 256)), 256, 0, s>>>(sf, M, G, AM, nwords,
+                                                                             reinterpret_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_scales(const int32_t* packed, int M, int G, uint8_t* sf, hipStream_t s) {
+  const int AM = (M + 3) / 4 * 4;
+  const long long nwords = (long long)((G + 3) / 4) * AM;
+  if (nwords == 0 || M == 0) return hipSuccess;
+  unpack_scales_kernel<<<dim3((unsigned)((nwords + 255) / 256)), 256, 0, s>>>(
+      reinterpret_cast<const uint32_t*>(packed), M, G, AM, nwords, sf);
+  return hipGetLastError();
+}
+
 }  // namespace moe

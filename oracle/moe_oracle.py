@@ -261,6 +261,35 @@ def quantize_act(x_bf16_bits: np.ndarray):
     return requant_1x128(decode_bf16(x_bf16_bits))
 
 
+def pack_ue8m0(sf: np.ndarray) -> np.ndarray:
+    """UE8M0 bytes [M, G] -> packed int32 storage [ceil(G/4), aligned_M] (aligned_M = M rounded up to 4).
+
+    The packed scale tensor of "DSV4 o_proj: fuse fp8/UE8M0 quantize into o_a proj" (the
+    o_a FP8-output tactic's checks): int32, shape (M, ceil(G/4)), MN-major stride
+    (1, aligned_M), padding zeroed.  Word (m, j) holds groups 4j .. 4j+3 of row m, group
+    4j + b in byte b (little-endian; the byte order is not printed on the page).  The
+    returned array is the storage: element [j, m] is word (m, j).
+    """
+    sf = np.asarray(sf, dtype=np.uint8)
+    m, g = sf.shape
+    am, nw = (m + 3) // 4 * 4, (g + 3) // 4
+    out = np.zeros((nw, am), dtype=np.uint32)
+    for j in range(nw):
+        for b in range(4):
+            if 4 * j + b < g:
+                out[j, :m] |= sf[:, 4 * j + b].astype(np.uint32) << np.uint32(8 * b)
+    return out.view(np.int32)
+
+
+def unpack_ue8m0(packed: np.ndarray, m: int, g: int) -> np.ndarray:
+    """Inverse of pack_ue8m0: storage [ceil(G/4), aligned_M] int32 -> UE8M0 bytes [M, G]."""
+    w = np.asarray(packed).view(np.uint32)
+    sf = np.zeros((m, g), dtype=np.uint8)
+    for k in range(g):
+        sf[:, k] = (w[k // 4, :m] >> np.uint32(8 * (k % 4))) & np.uint32(0xFF)
+    return sf
+
+
 def expert_rows(d, inputs, e: int, tokens: np.ndarray):
     """FC1 -> activation -> requant -> FC2 for rows of local expert e whose tokens are given.
 

@@ -130,3 +130,12 @@ def test_quantize_act_validation(L):
     assert L.moe_quantize_act(ctypes.byref(d), P(0x1008), P(0x2000), P(0x3000), None) == B.MOE_ERR_MISALIGNED
     d.hidden = 100
     assert L.moe_quantize_act(ctypes.byref(d), P(0x1000), P(0x2000), P(0x3000), None) == B.MOE_ERR_INVALID_DESC
+
+
+def test_pack_scales_validation(L):
+    P = ctypes.c_void_p
+    assert L.moe_pack_scales(-1, 4, P(0x1000), P(0x2000), None) == B.MOE_ERR_INVALID_DESC
+    assert L.moe_pack_scales(4, 0, P(0x1000), P(0x2000), None) == B.MOE_ERR_INVALID_DESC
+    assert L.moe_pack_scales(4, 4, None, P(0x2000), None) == B.MOE_ERR_NULL
+    assert L.moe_unpack_scales(4, 4, P(0x2002), P(0x1000), None) == B.MOE_ERR_MISALIGNED
+    assert L.moe_pack_scales(0, 4, None, None, None) == B.MOE_OK

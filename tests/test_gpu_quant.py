@@ -69,3 +69,28 @@ def test_quantize_fullsize(cfg):
     rows = np.random.default_rng(41).choice(w.tokens, size=min(16, w.tokens), replace=False)
     rq, rsf = O.quantize_act(inp["x_bf16"][rows])
     assert np.array_equal(q[rows], rq) and np.array_equal(sf[rows], rsf)
+
+
+@pytest.mark.parametrize("m,g", [(1, 1), (3, 4), (5, 6), (37, 3), (130, 16), (4096, 56)])
+def test_pack_unpack_scales_bit_exact(m, g):
+    sf = np.random.default_rng(m + 7 * g).integers(0, 255, (m, g)).astype(np.uint8)
+    ref = O.pack_ue8m0(sf)
+    dsf = torch.from_numpy(sf).cuda()
+    packed = torch.full((ref.size,), -1, dtype=torch.int32, device="cuda")  # poisoned: padding must be written
+    B.moe_pack_scales(m, g, dsf, packed)
+    back = torch.full((m, g), 0xAB, dtype=torch.uint8, device="cuda")
+    B.moe_unpack_scales(m, g, packed, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), ref.ravel())
+    assert np.array_equal(back.cpu().numpy(), sf)
+
+
+def test_quantize_then_pack_matches_oracle():
+    w = synth.shrink(synth.workload("decode"), tokens=61)
+    inp = synth.generate(w, with_bf16=True)
+    q, sf = _run(inp["x_bf16"])
+    g = w.hidden // 128
+    packed = torch.empty(((g + 3) // 4) * ((w.tokens + 3) // 4 * 4), dtype=torch.int32, device="cuda")
+    B.moe_pack_scales(w.tokens, g, torch.from_numpy(sf).cuda(), packed)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), O.pack_ue8m0(O.quantize_act(inp["x_bf16"])[1]).ravel())

@@ -50,3 +50,31 @@ def test_generator_bf16_is_the_quantised_input():
     inp = synth.generate(w, with_bf16=True)
     q, sf = O.quantize_act(inp["x_bf16"])
     assert np.array_equal(q, inp["x"]) and np.array_equal(sf, inp["x_sf"])
+
+
+def test_pack_ue8m0_worked_example():
+    # M = 5 rows, G = 6 groups: aligned M = 8, two words per row; rows 5..7 and the upper
+    # half of each row's second word are padding (zero)
+    sf = np.arange(30, dtype=np.uint8).reshape(5, 6) + 100
+    st = O.pack_ue8m0(sf)
+    assert st.shape == (2, 8) and st.dtype == np.int32
+    for m in range(5):
+        w0 = int(sf[m, 0]) | int(sf[m, 1]) << 8 | int(sf[m, 2]) << 16 | int(sf[m, 3]) << 24
+        w1 = int(sf[m, 4]) | int(sf[m, 5]) << 8
+        assert int(st[0, m].view(np.uint32)) == w0 and int(st[1, m].view(np.uint32)) == w1
+    assert not st[:, 5:].any()
+    # the storage viewed with the printed shape (M, ceil(G/4)) and stride (1, aligned_M)
+    t = torch.as_strided(torch.from_numpy(st.ravel().copy()), (5, 2), (1, 8))
+    assert int(t[3, 1]) == int(st[1, 3]) and int(t[4, 0]) == int(st[0, 4])
+
+
+@pytest.mark.parametrize("m,g", [(1, 1), (3, 4), (4, 5), (7, 56), (130, 16)])
+def test_pack_unpack_round_trip(m, g):
+    sf = np.random.default_rng(m * 100 + g).integers(0, 255, (m, g)).astype(np.uint8)
+    st = O.pack_ue8m0(sf)
+    assert st.shape == ((g + 3) // 4, (m + 3) // 4 * 4)
+    assert np.array_equal(O.unpack_ue8m0(st, m, g), sf)
+    w = st.view(np.uint32)
+    assert not w[:, m:].any()  # padding rows
+    if g % 4:
+        assert not (w[-1, :m] >> np.uint32(8 * (g % 4))).any()  # padding bytes
