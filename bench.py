@@ -37,7 +37,7 @@ def source_hash() -> str:
 def algorithmic(w, R, active, counts):
     """Useful FLOPs and bytes of the layer and of FC1 / FC2 for this routing."""
     H, I, T, E = w.hidden, w.inter, w.tokens, w.num_experts
-    if w.weight_format == "fp8":
+    if w.weight_format != "mxfp4":
         wb = lambda n, k: n * k * (1 + 1 / 16384)
     else:
         wb = lambda n, k: n * k * (0.5 + 1 / 32)
@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--config", default="oai", help="workload name or index (tiny, oai, decode, prefill_zipf, "
                                                      "mxfp4_large)")
     ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--weights", choices=["fp8", "fp8e5m2", "mxfp4"], default=None,
+                    help="replace the workload's weight format (FP8 E4M3, FP8 E5M2 or MXFP4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=20, help="timed launches of the dominant kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -116,6 +118,8 @@ def main():
         __graft_entry__.build()
     cfg = int(args.config) if args.config.isdigit() else args.config
     w = synth.workload(cfg)
+    if args.weights and args.weights != w.weight_format:
+        w = synth.shrink(w, weight_format=args.weights, name=f"{w.name}/{args.weights}")
     t0 = time.time()
     inp = synth.generate(w)
     print(f"[bench] generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -220,7 +224,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if w.weight_format == "fp8" else "fp8xfp4",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4" if w.weight_format == "mxfp4" else "fp8",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "inter": w.inter,
                    "experts": w.num_experts, "local_experts": EL, "topk": k, "activation": w.activation,

@@ -27,12 +27,13 @@
  *   - Layouts are row-major and dense:
  *       logits      float32 [T, E_tot]
  *       x           E4M3 bytes [T, H]            x_sf   UE8M0 bytes [T, H/128]
- *       w1 (fp8)    E4M3 bytes [E_loc, 2I, H]    w1_sf  UE8M0 [E_loc, 2I/128, H/128]
- *       w1 (mxfp4)  E2M1 pairs [E_loc, 2I, H/2]  w1_sf  UE8M0 [E_loc, 2I, H/32]
- *       w2 (fp8)    E4M3 bytes [E_loc, H, I]     w2_sf  UE8M0 [E_loc, H/128, I/128]
- *       w2 (mxfp4)  E2M1 pairs [E_loc, H, I/2]   w2_sf  UE8M0 [E_loc, H, I/32]
+ *       w1 (fp8)    E4M3 or E5M2 bytes [E_loc, 2I, H]  w1_sf  UE8M0 [E_loc, 2I/128, H/128]
+ *       w1 (mxfp4)  E2M1 pairs [E_loc, 2I, H/2]        w1_sf  UE8M0 [E_loc, 2I, H/32]
+ *       w2 (fp8)    E4M3 or E5M2 bytes [E_loc, H, I]   w2_sf  UE8M0 [E_loc, H/128, I/128]
+ *       w2 (mxfp4)  E2M1 pairs [E_loc, H, I/2]         w2_sf  UE8M0 [E_loc, H, I/32]
  *     W1 rows [0, I) are the gate projection and rows [I, 2I) the up projection.
- *     MXFP4: element 2i of a K-row is the low nibble of byte i.  E4M3 is OCP E4M3FN.
+ *     MXFP4: element 2i of a K-row is the low nibble of byte i.  E4M3 is OCP E4M3FN,
+ *     E5M2 is OCP E5M2 (weights only; x and h are always E4M3).
  *     UE8M0 byte b is 2^(b-127); 255 (NaN) is not allowed.
  *       topk_ids    int32 [T, k]  slot j = j-th largest logit (ties: lower expert id)
  *       topk_w      float32 [T, k] softmax over the k chosen logits (computed in fp64)
@@ -85,8 +86,10 @@ typedef enum {
 /* Activation names follow the pages' API: "swiglu" and "swigluoai". */
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
 
-/* Weight formats: FP8 E4M3 with 128x128 UE8M0 block scales, or MXFP4 (E2M1, UE8M0 per 32 along K). */
-typedef enum { MOE_W_FP8_E4M3_B128 = 0, MOE_W_MXFP4_E2M1_B32 = 1 } moe_wfmt;
+/* Weight formats: FP8 E4M3 or E5M2 with 128x128 UE8M0 block scales, or MXFP4 (E2M1, UE8M0
+ * per 32 along K).  The FP8 weight formats are the ones the Hopper CuTeDSL MegaMoE kernel
+ * takes (Pull Style Cutedsl Megakernel, Layout section); the activations stay E4M3. */
+typedef enum { MOE_W_FP8_E4M3_B128 = 0, MOE_W_MXFP4_E2M1_B32 = 1, MOE_W_FP8_E5M2_B128 = 2 } moe_wfmt;
 
 typedef struct {
   int32_t num_tokens;     /* T >= 0 */

@@ -84,7 +84,9 @@ struct Cfg {
   static constexpr int WN = NW / WM;                        // waves along N
   static constexpr int MI = WTM / 32;                       // 32-row tiles per wave
   static constexpr int A_ROWB = BK;                         // bytes per activation row per stage
-  static constexpr int B_ROWB = WFMT == 0 ? BK : BK / 2;    // bytes per weight row per stage
+  static constexpr int B_ROWB = WFMT == 1 ? BK / 2 : BK;    // bytes per weight row per stage
+  // weight operand format code of the scaled MFMA: E4M3 0, E5M2 1, E2M1 4
+  static constexpr int WCODE = WFMT == 1 ? 4 : (WFMT == 2 ? 1 : 0);
   static constexpr int A_BYTES = BM * A_ROWB;
   static constexpr int B_BYTES = BN * B_ROWB;
   static constexpr int S_BYTES = WFMT == 1 ? NW * 256 : 0;  // MXFP4 scale dwords (64 rows per wave)
@@ -102,7 +104,7 @@ struct Cfg {
   static_assert(WM * WN == NW && NT >= 1 && (MODE == 2 || NT % 2 == 0), "waves must cover the tile");
   static_assert(A_INSTR >= 1 && B_DMA >= 1 && B_DMA * NW * 1024 == B_BYTES, "");
   static_assert(A_INSTR >= NW ? A_DMA * NW == A_INSTR : NW % A_INSTR == 0, "");
-  static_assert(WFMT == 0 || BN <= NW * 64, "one scale DMA per wave covers 64 weight rows");
+  static_assert(WFMT != 1 || BN <= NW * 64, "one scale DMA per wave covers 64 weight rows");
   static_assert(PIPE != 1 || NSTAGE >= 3, "stage-ahead fragments need the next stage resident");
   static_assert(PIPE != 2 || BK == 128, "the half-step pipeline splits 128-wide stages");
 };
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   // FP8 weight scales of the tile's two 128-row blocks (FC1: gate n0/128 and up (I+n0)/128;
   // FC2: n0/128 and n0/128 + 1, clamped), loaded now and written to LDS after the DMA issue
   const uint8_t* bsf_e = g.B_sf + (long long)e * g.bsf_estride;
-  const bool bsf_mine = WFMT == 0 && tid < 2 * nk128;
+  const bool bsf_mine = WFMT != 1 && tid < 2 * nk128;
   int bsf_v = 0;
   if (bsf_mine) {
     const int blk = tid / nk128, ks = tid - blk * nk128;
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
     const int rr = n0 + n;
     return rr < g.N ? rr : g.N - 1;
   };
-  const uint32_t b_ld = WFMT == 0 ? g.K : g.K / 2;
+  const uint32_t b_ld = WFMT == 1 ? g.K / 2 : g.K;
   uint32_t b_off[C::B_DMA];
 #pragma unroll
   for (int j = 0; j < C::B_DMA; ++j) {
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi) {
     a_lds[hi] = ra * C::A_ROWB + (((2 * hi + kb) ^ swz<C::A_CPR>(ra)) << 4);
-    b_lds[hi] = WFMT == 0 ? rb * C::B_ROWB + (((2 * hi + kb) ^ swz<C::B_CPR>(rb)) << 4)
+    b_lds[hi] = WFMT != 1 ? rb * C::B_ROWB + (((2 * hi + kb) ^ swz<C::B_CPR>(rb)) << 4)
                            : rb * C::B_ROWB + ((kb ^ swz<C::B_CPR>(rb)) << 4);
   }
 
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) f.sa[mi] = s_asf[(ra + mi * 32) * nk128 + k128];
     int sbu0 = 0, sbu1 = 0;
-    if (WFMT == 0) {  // one weight scale per 128x128 block
+    if (WFMT != 1) {  // one weight scale per 128x128 block
       if (MODE == 1) { sbu0 = s_bsf[k128]; sbu1 = s_bsf[nk128 + k128]; }
       else { sbu0 = s_bsf[(wn * (BN / C::WN)) / 128 * nk128 + k128]; sbu1 = sbu0; }
     }
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
 #pragma unroll
       for (int ct = 0; ct < C::NT; ++ct) {
         const int d = bdelta(ct);
-        if (WFMT == 0) {
+        if (WFMT != 1) {
           const bool flip = C::B_CPR == 8 && ((h ^ (d / 32)) & 1);
           const int imm = d * C::B_ROWB;
           const uint4 lo = lds16(sb_ + (flip ? b_lds[0] ^ 64u : b_lds[0]) + imm);
@@ -419,10 +421,10 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
         for (int mi = 0; mi < NL; ++mi)
           acc[mi][ct] = MODE == 1
                             ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[h][ct], f.a[h][mi], acc[mi][ct],
-                                                                              WFMT == 0 ? 0 : 4, 0, 0, f.sb[h][ct],
+                                                                              C::WCODE, 0, 0, f.sb[h][ct],
                                                                               0, f.sa[mi])
                             : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[h][mi], f.b[h][ct], acc[mi][ct], 0,
-                                                                              WFMT == 0 ? 0 : 4, 0, f.sa[mi], 0,
+                                                                              C::WCODE, 0, f.sa[mi], 0,
                                                                               f.sb[h][ct]);
   };
   const int live_tiles = min(C::MI, max(0, (rows - wm * WTM + 31) / 32));
@@ -653,23 +655,26 @@ static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int MODE>
-static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_t grid, hipStream_t s) {
-  if (variant == 1) {
-    return wfmt == 0 ? launch_one<MODE, 0, 256, 256, 128, 2, 8, 64, 2>(a, grid, s)
-                     : launch_one<MODE, 1, 256, 256, 128, 2, 8, 64, 2>(a, grid, s);
-  }
+template <int MODE, int WFMT>
+static hipError_t launch_variant_w(const GemmArgs& a, int variant, size_t grid, hipStream_t s) {
+  if (variant == 1) return launch_one<MODE, WFMT, 256, 256, 128, 2, 8, 64, 2>(a, grid, s);
   if (variant == 2) {
-    return wfmt == 0 ? launch_one<MODE, 0, 32, 256, 128, 2, 4, 32, 2>(a, grid, s)
-                     : launch_one<MODE, 1, 32, 256, 128, 3, 4, 32, 2>(a, grid, s);
+    if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 32, 256, 128, 3, 4, 32, 2>(a, grid, s);
+    else return launch_one<MODE, WFMT, 32, 256, 128, 2, 4, 32, 2>(a, grid, s);
   }
   // small experts: two workgroups fit one CU (<= 80 KB of LDS each) so one streams weights
   // while the other is in its prologue or epilogue; FC2 tiles are 128 columns wide
-  if (MODE == 2)
-    return wfmt == 0 ? launch_one<MODE, 0, 128, 128, 128, 2, 4, 64, 0>(a, grid, s)
-                     : launch_one<MODE, 1, 128, 128, 128, 2, 4, 64, 0>(a, grid, s);
-  return wfmt == 0 ? launch_one<MODE, 0, 128, 256, 64, 3, 4, 64, 0>(a, grid, s)
-                   : launch_one<MODE, 1, 128, 256, 64, 4, 4, 64, 0>(a, grid, s);
+  if constexpr (MODE == 2) return launch_one<MODE, WFMT, 128, 128, 128, 2, 4, 64, 0>(a, grid, s);
+  else if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 128, 256, 64, 4, 4, 64, 0>(a, grid, s);
+  else return launch_one<MODE, WFMT, 128, 256, 64, 3, 4, 64, 0>(a, grid, s);
+}
+
+// weight formats: 0 FP8 E4M3 with 128x128 scales, 1 MXFP4, 2 FP8 E5M2 with 128x128 scales
+template <int MODE>
+static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_t grid, hipStream_t s) {
+  if (wfmt == 1) return launch_variant_w<MODE, 1>(a, variant, grid, s);
+  if (wfmt == 2) return launch_variant_w<MODE, 2>(a, variant, grid, s);
+  return launch_variant_w<MODE, 0>(a, variant, grid, s);
 }
 
 hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
@@ -679,8 +684,8 @@ hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint
   a.A = x; a.A_sf = x_sf; a.row_to_slot = row_to_slot; a.B = w1; a.B_sf = w1_sf;
   a.offsets = offsets; a.plan = plan_ready ? plan : nullptr; a.h = h; a.h_sf = h_sf;
   a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.n_tiles = sh.I / 128;
-  a.b_estride = sh.wfmt == 0 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
-  a.bsf_estride = sh.wfmt == 0 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
+  a.b_estride = sh.wfmt != 1 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
+  a.bsf_estride = sh.wfmt != 1 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
   a.act = sh.act; a.clamp = sh.clamp; a.alpha = sh.alpha; a.bias = sh.bias;
   const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
   if (grid == 0) return hipSuccess;
@@ -695,8 +700,8 @@ hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint
   a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets; a.plan = plan_ready ? plan : nullptr;
   a.y2 = y2;
   a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL;
-  a.b_estride = sh.wfmt == 0 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
-  a.bsf_estride = sh.wfmt == 0 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
+  a.b_estride = sh.wfmt != 1 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
+  a.bsf_estride = sh.wfmt != 1 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
   const int bn = variant == 0 ? 128 : 256;
   a.n_tiles = (sh.H + bn - 1) / bn;
   const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;

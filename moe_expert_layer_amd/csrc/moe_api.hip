@@ -93,7 +93,8 @@ moe_status check_desc(const moe_layer_desc* d) {
     return fail(MOE_ERR_INVALID_DESC, "num_tokens * topk must be < 2^31");
   if ((long long)d->num_tokens * d->topk * d->hidden >= (1LL << 46))
     return fail(MOE_ERR_INVALID_DESC, "num_tokens * topk * hidden too large");
-  if (d->weight_format != MOE_W_FP8_E4M3_B128 && d->weight_format != MOE_W_MXFP4_E2M1_B32)
+  if (d->weight_format != MOE_W_FP8_E4M3_B128 && d->weight_format != MOE_W_MXFP4_E2M1_B32 &&
+      d->weight_format != MOE_W_FP8_E5M2_B128)
     return fail(MOE_ERR_INVALID_DESC, "weight_format %d unknown", d->weight_format);
   if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_SWIGLU_OAI)
     return fail(MOE_ERR_INVALID_DESC, "activation %d unknown", d->activation);

@@ -14,7 +14,7 @@ constexpr int kPermSmallBuckets = 257;  // ... and at most 256 local experts
 
 struct Shape {
   int T, H, I, E, e0, EL, k;
-  int wfmt;  // 0 fp8 block-128, 1 mxfp4
+  int wfmt;  // 0 E4M3 block-128, 1 mxfp4, 2 E5M2 block-128
   int act;   // 0 swiglu, 1 oai
   float clamp, alpha, bias;
 };

@@ -46,7 +46,7 @@ class Workload:
     act_clamp: float
     act_alpha: float
     act_up_bias: float
-    weight_format: str  # "fp8" | "mxfp4"
+    weight_format: str  # "fp8" (E4M3) | "fp8e5m2" | "mxfp4"
     routing: str  # "normal" | "zipf"
     zipf_s: float
     seed: int
@@ -101,25 +101,31 @@ def _pow2_exponent_for(amax: np.ndarray, top: float) -> np.ndarray:
     return e
 
 
-def _to_e4m3_bytes(v: np.ndarray) -> np.ndarray:
+_FP8 = {"e4m3": (torch.float8_e4m3fn, 448.0), "e5m2": (torch.float8_e5m2, 57344.0)}
+
+
+def _to_fp8_bytes(v: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
     t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32))
-    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return t.to(_FP8[fmt][0]).view(torch.uint8).numpy()
 
 
-def _quant_fp8_blocks(v: np.ndarray, br: int, bc: int):
-    """v [N, K] float32 -> E4M3 bytes [N, K] and UE8M0 bytes [ceil(N/br), K/bc] (block br x bc)."""
+def _quant_fp8_blocks(v: np.ndarray, br: int, bc: int, fmt: str = "e4m3"):
+    """v [N, K] float32 -> FP8 bytes [N, K] and UE8M0 bytes [ceil(N/br), K/bc] (block br x bc).
+
+    The block scale is the smallest power of two that brings the block's amax within the
+    format's largest finite value (448 for E4M3, 57344 for E5M2)."""
     n, kk = v.shape
     nb = (n + br - 1) // br
     pad = nb * br - n
     vp = np.pad(v, ((0, pad), (0, 0))) if pad else v
     blk = np.abs(vp.reshape(nb, br, kk // bc, bc)).max(axis=(1, 3)).astype(np.float64)
-    e = _pow2_exponent_for(blk, 448.0)
+    e = _pow2_exponent_for(blk, _FP8[fmt][1])
     e = np.where(blk == 0, 0, e)
     e = np.clip(e, -127, 127)
     sf = (e + 127).astype(np.uint8)
     inv = np.ldexp(np.float32(1.0), (-e).astype(np.int32)).astype(np.float32)
     scaled = (vp.reshape(nb, br, kk // bc, bc) * inv[:, None, :, None]).reshape(nb * br, kk)
-    q = _to_e4m3_bytes(scaled[:n])
+    q = _to_fp8_bytes(scaled[:n], fmt)
     return q, sf
 
 
@@ -173,7 +179,10 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: 
     if with_bf16:
         out["x_bf16"] = (xf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     del xf
-    fp8 = w.weight_format == "fp8"
+    if w.weight_format not in ("fp8", "fp8e5m2", "mxfp4"):
+        raise ValueError(f"unknown weight format {w.weight_format}")
+    fp8 = w.weight_format != "mxfp4"
+    f8 = "e5m2" if w.weight_format == "fp8e5m2" else "e4m3"
     w1 = np.empty((EL, 2 * I, H if fp8 else H // 2), np.uint8)
     w1_sf = np.empty((EL, 2 * I // 128, H // 128) if fp8 else (EL, 2 * I, H // 32), np.uint8)
     w2 = np.empty((EL, H, I if fp8 else I // 2), np.uint8)
@@ -183,7 +192,7 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: 
         for which, shape, dst, dsf in ((0, (2 * I, H), w1, w1_sf), (1, (H, I), w2, w2_sf)):
             a = rng(2 + 2 * e + which).standard_normal(shape, dtype=np.float32)
             a *= np.float32(0.02)
-            q, s = _quant_fp8_blocks(a, 128, 128) if fp8 else _quant_mxfp4(a)
+            q, s = _quant_fp8_blocks(a, 128, 128, f8) if fp8 else _quant_mxfp4(a)
             dst[e], dsf[e] = q, s
 
     with cf.ThreadPoolExecutor(max_workers=max(1, threads)) as ex:

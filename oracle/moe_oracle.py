@@ -11,7 +11,7 @@ one GPU's share of the experts, written from the pages' description of the fused
   route      top-k of each token's routing logits, softmax weights over the k chosen
   permute    group the local (token, slot) pairs by expert, stable by slot id
   FC1        gate/up projection of the FP8 E4M3 activations with 1x128 UE8M0 scales
-             against FP8 E4M3 weights with 128x128 UE8M0 block scales (or MXFP4)
+             against FP8 (E4M3 or E5M2) weights with 128x128 UE8M0 block scales (or MXFP4)
   activation SwiGLU, or parameterised OAI-SwiGLU (clamp, sigmoid alpha, up bias)
   requant    the intermediate back to FP8 E4M3 with one UE8M0 scale per 1x128 block
   quantize   (input side) bf16 activations to FP8 E4M3 with the same 1x128 UE8M0 rule
@@ -29,7 +29,8 @@ Sources (pages of the study, cited by title and section):
   * "DSV4 o_proj: fuse fp8/UE8M0 quantize into o_a proj" (TensorRT-LLM PR #16346),
     Description: a 1x128 FP8 E4M3 quantisation with UE8M0 scales, amax per block.
   * "Pull Style Cutedsl Megakernel" (FlashInfer skill page), Layout: the fused
-    layer is FC1 -> FC2 -> top-k reduce.
+    layer is FC1 -> FC2 -> top-k reduce, and the Hopper kernel takes E4M3 or E5M2
+    weights.
 
 Readings where the pages are silent (each is listed with its reason in the design
 notes): routing is top-k by (logit descending, expert id ascending) with an fp64
@@ -50,7 +51,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "decode_e4m3", "decode_ue8m0", "decode_e2m1", "encode_e4m3_rne", "bf16_rne_bits",
+    "decode_e4m3", "decode_e5m2", "decode_ue8m0", "decode_e2m1", "encode_e4m3_rne", "bf16_rne_bits",
     "dequant_act", "dequant_weight", "route", "permute", "activation", "requant_1x128",
     "expert_rows", "combine", "layer", "layer_tokens",
 ]
@@ -68,6 +69,18 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
     out = np.where(s == 1, -mag, mag)
     return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def decode_e5m2(codes: np.ndarray) -> np.ndarray:
+    """E5M2 byte -> float64: sign, 5-bit exponent (bias 15), 2-bit mantissa; exponent 31 is
+    infinity (mantissa 0) or NaN, exponent 0 is subnormal (m/4 * 2**-14)."""
+    c = codes.astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 2) & 0x1F
+    m = c & 3
+    mag = np.where(e == 0, np.ldexp(m / 4.0, -14), np.ldexp(1.0 + m / 4.0, e - 15))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return np.where(s == 1, -mag, mag)
 
 
 def decode_ue8m0(b: np.ndarray) -> np.ndarray:
@@ -133,12 +146,14 @@ def dequant_act(x: np.ndarray, x_sf: np.ndarray) -> np.ndarray:
 def dequant_weight(w: np.ndarray, sf: np.ndarray, fmt: str, rows: int, cols: int) -> np.ndarray:
     """One expert's weight -> float64 [rows, cols] (K = cols contiguous).
 
-    fp8:   E4M3 bytes [rows, cols], UE8M0 per 128x128 block [rows/128, cols/128].
-    mxfp4: packed E2M1 [rows, cols/2] (element 2i low nibble), UE8M0 per 1x32 [rows, cols/32].
+    fp8:     E4M3 bytes [rows, cols], UE8M0 per 128x128 block [rows/128, cols/128].
+    fp8e5m2: E5M2 bytes, the same 128x128 block scales.
+    mxfp4:   packed E2M1 [rows, cols/2] (element 2i low nibble), UE8M0 per 1x32 [rows, cols/32].
     """
-    if fmt == "fp8":
+    if fmt in ("fp8", "fp8e5m2"):
         s = decode_ue8m0(sf)
-        v = decode_e4m3(w).reshape(rows // 128, 128, cols // 128, 128)
+        dec = decode_e4m3 if fmt == "fp8" else decode_e5m2
+        v = dec(w).reshape(rows // 128, 128, cols // 128, 128)
         return (v * s[:, None, :, None]).reshape(rows, cols)
     if fmt == "mxfp4":
         vals = np.empty((rows, cols), dtype=np.float64)

@@ -24,7 +24,14 @@ def e4m3_table():
     return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
+def e5m2_table():
+    """code -> value for all 256 E5M2 codes (torch decode; +-inf and NaN at exponent 31)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+
+
 _E4 = e4m3_table()
+_E5 = e5m2_table()
 _FINITE = [(c, Fraction(float(_E4[c]))) for c in range(256) if not math.isnan(_E4[c])]
 
 
@@ -77,6 +84,10 @@ def decode_e4m3_torch(codes: np.ndarray) -> np.ndarray:
     return _E4[codes.astype(np.int64)]
 
 
+def decode_e5m2_torch(codes: np.ndarray) -> np.ndarray:
+    return _E5[codes.astype(np.int64)]
+
+
 def sigmoid(z: float) -> float:
     if z >= 0:
         return 1.0 / (1.0 + math.exp(-z))
@@ -95,8 +106,8 @@ def act_scalar(g, u, kind, clamp, alpha, bias):
 def weight_dense(w, sf, fmt, rows, cols):
     """Dequantise one expert's weight with explicit loops over blocks."""
     out = np.zeros((rows, cols))
-    if fmt == "fp8":
-        vals = decode_e4m3_torch(w)
+    if fmt in ("fp8", "fp8e5m2"):
+        vals = decode_e4m3_torch(w) if fmt == "fp8" else decode_e5m2_torch(w)
         for rb in range(rows // 128):
             for cb in range(cols // 128):
                 s = 2.0 ** (int(sf[rb, cb]) - 127)

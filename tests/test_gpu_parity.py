@@ -37,6 +37,9 @@ def _small_cases():
                                     num_experts=64, num_local=16, topk=6, seed=9)),
         ("mxfp4_small", synth.shrink(synth.workload("mxfp4_large"), tokens=200, hidden=512, inter=384,
                                      num_experts=16, num_local=8, topk=4, seed=10)),
+        # E5M2 weights (activations stay E4M3): MFMA weight-operand format 1
+        ("e5m2_small", synth.shrink(oai, tokens=300, hidden=768, inter=384, num_experts=16, num_local=8, topk=4,
+                                    weight_format="fp8e5m2", seed=15)),
         ("top1", synth.shrink(tiny, tokens=130, topk=1, seed=11)),
         ("k16_e1024", synth.shrink(tiny, tokens=40, num_experts=1024, local_begin=1000, num_local=24, topk=16,
                                    seed=12)),
@@ -74,7 +77,8 @@ def test_layer_parity_small(name, w):
 
 
 @pytest.mark.parametrize("variant", [0, 1, 2])
-@pytest.mark.parametrize("name", ["ragged_oai", "ragged_h384_share", "zipf_small", "mxfp4_small", "k16_e1024"])
+@pytest.mark.parametrize("name", ["ragged_oai", "ragged_h384_share", "zipf_small", "mxfp4_small", "e5m2_small",
+                                  "k16_e1024"])
 def test_layer_parity_forced_variant(name, variant):
     w = dict(_small_cases())[name]
     G.say(f"[variant] {name} variant={variant}")
@@ -97,29 +101,31 @@ def test_run_twice_bit_identical():
     assert np.array_equal(a["y_bf16"], b["y_bf16"])
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp8e5m2"])
 @pytest.mark.parametrize("variant", [-1, 0, 1, 2])
-def test_exact_integer_layer_bit_exact(variant):
+def test_exact_integer_layer_bit_exact(variant, fmt):
     """Small-integer operands, unit scales, top-1, OAI with alpha 0: every partial sum is exact in
     fp32 (x, W2 in {-1, 0, 1}; W1 rows with at most 4 non-zeros so |g|, |u| <= 4 and h = g*u/2 is a
     half-integer <= 8 that the requant reproduces exactly), so the GPU output equals the oracle bit for bit."""
     rng = np.random.default_rng(9)
     T, H, I, E = 200, 256, 256, 4
     w = synth.shrink(synth.workload("tiny"), tokens=T, hidden=H, inter=I, num_experts=E, num_local=E, topk=1,
-                     activation="swigluoai", act_clamp=np.inf, act_alpha=0.0, act_up_bias=0.0)
+                     activation="swigluoai", act_clamp=np.inf, act_alpha=0.0, act_up_bias=0.0, weight_format=fmt)
     ONE, MONE = 0x38, 0xB8  # E4M3 codes of +1 and -1
+    WONE, WMONE = (0x38, 0xB8) if fmt == "fp8" else (0x3C, 0xBC)  # the weights' codes of +1 and -1
 
-    def pm1(shape, p_zero):
-        v = rng.choice([MONE, 0, ONE], size=shape, p=[(1 - p_zero) / 2, p_zero, (1 - p_zero) / 2])
+    def pm1(shape, p_zero, one=ONE, mone=MONE):
+        v = rng.choice([mone, 0, one], size=shape, p=[(1 - p_zero) / 2, p_zero, (1 - p_zero) / 2])
         return v.astype(np.uint8)
 
     w1 = np.zeros((E, 2 * I, H), np.uint8)
     for e in range(E):
         for n in range(2 * I):
             cols = rng.choice(H, size=4, replace=False)
-            w1[e, n, cols] = rng.choice([MONE, ONE], size=4)
+            w1[e, n, cols] = rng.choice([WMONE, WONE], size=4)
     inp = {"logits": rng.standard_normal((T, E)).astype(np.float32), "x": pm1((T, H), 0.3),
            "x_sf": np.full((T, H // 128), 127, np.uint8), "w1": w1,
-           "w1_sf": np.full((E, 2 * I // 128, H // 128), 127, np.uint8), "w2": pm1((E, H, I), 0.3),
+           "w1_sf": np.full((E, 2 * I // 128, H // 128), 127, np.uint8), "w2": pm1((E, H, I), 0.3, WONE, WMONE),
            "w2_sf": np.full((E, H // 128, I // 128), 127, np.uint8)}
     ref = O.layer(w, inp)
     got = G.run_split(w, G.upload(inp), variant=variant)

@@ -20,6 +20,34 @@ def test_decode_e4m3_all_codes_match_torch():
     assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF]) and ours[0x7E] == 448.0
 
 
+def test_decode_e5m2_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e5m2(codes)
+    ref = brute.e5m2_table()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])  # includes +-inf at 0x7C / 0xFC
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+
+
+def test_decode_e5m2_hand_values():
+    # OCP FP8 E5M2: bias 15, largest finite 0x7B = 1.75 * 2**15, smallest subnormal 2**-16
+    v = O.decode_e5m2(np.array([0x3C, 0x3D, 0x7B, 0x01, 0x03, 0x04, 0x7C, 0xBC, 0x80], np.uint8))
+    assert list(v[:6]) == [1.0, 1.25, 57344.0, 2.0 ** -16, 3 * 2.0 ** -16, 2.0 ** -14]
+    assert v[6] == np.inf and v[7] == -1.0 and v[8] == 0.0 and np.signbit(v[8])
+
+
+def test_dequant_weight_e5m2_block_scales():
+    rng = np.random.default_rng(4)
+    w = (rng.integers(0, 0x7C, (256, 256)) | (rng.integers(0, 2, (256, 256)) << 7)).astype(np.uint8)
+    sf = rng.integers(110, 135, (2, 2), dtype=np.uint8)
+    ours = O.dequant_weight(w, sf, "fp8e5m2", 256, 256)
+    ref = brute.weight_dense(w, sf, "fp8e5m2", 256, 256)
+    assert np.array_equal(ours, ref)
+    # the same bytes read as E4M3 give different values: the format switch is live
+    assert not np.array_equal(ours, O.dequant_weight(w, sf, "fp8", 256, 256))
+
+
 def _midpoints_and_values():
     vals = np.unique(brute.e4m3_table()[:0x7F])  # non-negative finite values
     mids = (vals[1:] + vals[:-1]) / 2

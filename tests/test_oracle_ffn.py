@@ -87,6 +87,7 @@ def _tiny(**kw):
     _tiny(activation="swigluoai", act_clamp=7.0, act_alpha=1.702, act_up_bias=1.0, seed=11),
     _tiny(num_experts=8, local_begin=2, num_local=3, topk=3, seed=12),
     _tiny(weight_format="mxfp4", seed=13, tokens=4),
+    _tiny(weight_format="fp8e5m2", seed=14),
 ])
 def test_layer_matches_token_by_token_bruteforce(d):
     inp = synth.generate(d)
