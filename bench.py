@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--weights", choices=["fp8", "fp8e5m2", "mxfp4"], default=None,
                     help="replace the workload's weight format (FP8 E4M3, FP8 E5M2 or MXFP4)")
+    ap.add_argument("--scaling", choices=["block", "tensor"], default="block",
+                    help="blockwise UE8M0 scales, or one float32 scale per tensor (FP8 weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=20, help="timed launches of the dominant kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -120,6 +122,8 @@ def main():
     w = synth.workload(cfg)
     if args.weights and args.weights != w.weight_format:
         w = synth.shrink(w, weight_format=args.weights, name=f"{w.name}/{args.weights}")
+    if args.scaling == "tensor":
+        w = synth.tensor_scaled(w, name=f"{w.name}/tensor")
     t0 = time.time()
     inp = synth.generate(w)
     print(f"[bench] generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -202,15 +206,16 @@ def main():
     roof["traffic"] = traffic
 
     # input quantisation (bf16 -> E4M3 + 1x128 UE8M0) of this workload's activations, HBM-bound
+    dq = B.desc_from_workload(synth.shrink(w, scaling="block"), args.variant)
     xb = torch.randn((T, w.hidden), device="cuda").to(torch.bfloat16)
     xq = torch.empty((T, w.hidden), dtype=torch.uint8, device="cuda")
     xq_sf = torch.empty((T, w.hidden // 128), dtype=torch.uint8, device="cuda")
     for _ in range(3):
-        B.moe_quantize_act(d, xb, xq, xq_sf, stream=stream)
+        B.moe_quantize_act(dq, xb, xq, xq_sf, stream=stream)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.kernel_steps):
-        B.moe_quantize_act(d, xb, xq, xq_sf, stream=stream)
+        B.moe_quantize_act(dq, xb, xq, xq_sf, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
     q_ms = e0.elapsed_time(e1) / args.kernel_steps
@@ -228,7 +233,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "inter": w.inter,
                    "experts": w.num_experts, "local_experts": EL, "topk": k, "activation": w.activation,
-                   "weight_format": w.weight_format, "rows": R, "active_experts": active,
+                   "weight_format": w.weight_format, "scaling": w.scaling, "rows": R, "active_experts": active,
                    "parallelism": "one GPU's expert share", "weight_copies": len(wsets)},
         "tflops": round(tflops, 2), "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),

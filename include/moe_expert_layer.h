@@ -46,6 +46,15 @@
  *   - Requant rule: per 1x128 block, scale 2^e with the smallest integer e such that
  *     448 * 2^e >= amax (byte 127 for an all-zero block), codes = E4M3 round to
  *     nearest even of h * 2^-e.
+ *   - Per-tensor scaling (scale_mode = MOE_SCALE_TENSOR; FP8 weight formats only) replaces
+ *     every UE8M0 scale tensor with float32 scales (the Hopper kernel's per-tensor mode,
+ *     Pull Style Cutedsl Megakernel, Layout section):
+ *       x_sf        float32 [1]       x = code * x_sf[0]
+ *       w1_sf       float32 [E_loc]   W1[e] = code * w1_sf[e]   (w2_sf likewise)
+ *       h           E4M3 codes of h / h_scale, round to nearest even, saturated to +-448;
+ *                   h_scale (> 0, finite) is the static scale in the descriptor and
+ *                   h_sf is neither read nor written (it may be NULL)
+ *     Non-finite or non-positive tensor scales give unspecified results.
  *   - Logits must be finite; non-finite logits give unspecified routing.
  *   - Validation happens on the host before any launch; on error nothing is
  *     launched and a moe_status is returned (moe_last_error() has details).  A
@@ -71,7 +80,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -85,6 +94,9 @@ typedef enum {
 
 /* Activation names follow the pages' API: "swiglu" and "swigluoai". */
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
+
+/* Scaling: blockwise UE8M0 (the default) or one float32 scale per tensor (see above). */
+typedef enum { MOE_SCALE_BLOCK = 0, MOE_SCALE_TENSOR = 1 } moe_scale;
 
 /* Weight formats: FP8 E4M3 or E5M2 with 128x128 UE8M0 block scales, or MXFP4 (E2M1, UE8M0
  * per 32 along K).  The FP8 weight formats are the ones the Hopper CuTeDSL MegaMoE kernel
@@ -106,6 +118,8 @@ typedef struct {
   float act_up_bias;      /* OAI only: (up + up_bias); default 0.0 */
   int32_t variant;        /* GEMM tiles: -1 = heuristic; 0 = 128-row tiles; 1 = 256-row tiles;
                              2 = 32-row tiles */
+  int32_t scale_mode;     /* moe_scale; default MOE_SCALE_BLOCK */
+  float h_scale;          /* MOE_SCALE_TENSOR only: static scale of the intermediate h */
 } moe_layer_desc;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION at build time). */
@@ -117,8 +131,8 @@ const char* moe_status_str(int status);
 /* Details of the last error returned on the calling thread ("" when none). */
 const char* moe_last_error(void);
 
-/* Fill *desc with defaults: SwiGLU, FP8 weights, clamp +inf, alpha 1.0, up_bias 0.0,
- * variant -1, all sizes 0 (the pages' Compatibility section: the OAI parameters
+/* Fill *desc with defaults: SwiGLU, FP8 weights, blockwise scales, clamp +inf, alpha 1.0,
+ * up_bias 0.0, variant -1, h_scale 1.0, all sizes 0 (the pages' Compatibility section: the OAI parameters
  * default to the standard SwiGLU behaviour).  Host only. */
 moe_status moe_desc_defaults(moe_layer_desc* desc);
 
@@ -166,7 +180,8 @@ moe_status moe_layer(const moe_layer_desc* desc, const float* logits, const uint
  * (byte e + 127 clamped to [0, 254]; 127 for an all-zero block), codes E4M3
  * round-to-nearest-even of v * 2^-e.  Deterministic and exact for finite inputs.
  * Uses desc->num_tokens and desc->hidden; x_bf16 and x must be 16-byte aligned. No
- * workspace; asynchronous on `stream`. */
+ * workspace; asynchronous on `stream`.  Blockwise scaling only (MOE_ERR_UNSUPPORTED for
+ * MOE_SCALE_TENSOR, whose x scale is the caller's calibration). */
 moe_status moe_quantize_act(const moe_layer_desc* desc, const uint16_t* x_bf16, uint8_t* x, uint8_t* x_sf,
                             void* stream);
 

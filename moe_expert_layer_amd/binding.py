@@ -20,6 +20,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_INVALID_DESC, MOE_ERR_MISALIGNED, MOE_ERR_UNSUPPOR
 MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = 0, 1
 MOE_W_FP8_E4M3_B128, MOE_W_MXFP4_E2M1_B32, MOE_W_FP8_E5M2_B128 = 0, 1, 2
 ACTIVATIONS = {"swiglu": MOE_ACT_SWIGLU, "swigluoai": MOE_ACT_SWIGLU_OAI}
+MOE_SCALE_BLOCK, MOE_SCALE_TENSOR = 0, 1
+SCALINGS = {"block": MOE_SCALE_BLOCK, "tensor": MOE_SCALE_TENSOR}
 WEIGHT_FORMATS = {"fp8": MOE_W_FP8_E4M3_B128, "mxfp4": MOE_W_MXFP4_E2M1_B32, "fp8e5m2": MOE_W_FP8_E5M2_B128}
 
 
@@ -29,7 +31,7 @@ class MoeLayerDesc(ctypes.Structure):
         ("num_experts", ctypes.c_int32), ("local_begin", ctypes.c_int32), ("num_local", ctypes.c_int32),
         ("topk", ctypes.c_int32), ("weight_format", ctypes.c_int32), ("activation", ctypes.c_int32),
         ("act_clamp", ctypes.c_float), ("act_alpha", ctypes.c_float), ("act_up_bias", ctypes.c_float),
-        ("variant", ctypes.c_int32),
+        ("variant", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("h_scale", ctypes.c_float),
     ]
 
 
@@ -89,7 +91,8 @@ def _check(st: int):
 def make_desc(num_tokens: int, hidden: int, inter: int, num_experts: int, topk: int, local_begin: int = 0,
               num_local: Optional[int] = None, weight_format: str = "fp8", activation: str = "swiglu",
               activation_clamp: Optional[float] = None, activation_alpha: float = 1.0,
-              activation_up_bias: float = 0.0, variant: int = -1) -> MoeLayerDesc:
+              activation_up_bias: float = 0.0, variant: int = -1, scaling: str = "block",
+              h_scale: float = 1.0) -> MoeLayerDesc:
     """Descriptor with the pages' keyword names (activation, activation_clamp/alpha/up_bias)."""
     d = MoeLayerDesc()
     _check(lib().moe_desc_defaults(ctypes.byref(d)))
@@ -102,12 +105,15 @@ def make_desc(num_tokens: int, hidden: int, inter: int, num_experts: int, topk: 
     d.act_clamp = math.inf if activation_clamp is None else activation_clamp
     d.act_alpha, d.act_up_bias = activation_alpha, activation_up_bias
     d.variant = variant
+    d.scale_mode = SCALINGS[scaling]
+    d.h_scale = h_scale
     return d
 
 
 def desc_from_workload(w, variant: int = -1) -> MoeLayerDesc:
     return make_desc(w.tokens, w.hidden, w.inter, w.num_experts, w.topk, w.local_begin, w.num_local,
-                     w.weight_format, w.activation, w.act_clamp, w.act_alpha, w.act_up_bias, variant)
+                     w.weight_format, w.activation, w.act_clamp, w.act_alpha, w.act_up_bias, variant,
+                     getattr(w, "scaling", "block"), getattr(w, "h_scale", 1.0))
 
 
 def moe_workspace_size(desc: MoeLayerDesc) -> int:

@@ -72,6 +72,12 @@ struct GemmArgs {
   int n_tiles;
   int act;
   float clamp, alpha, bias;
+  // per-tensor scaling: the MFMAs run with unit scales and the accumulators are multiplied
+  // by (x scale or h_scale) * the expert's weight scale; FC1 quantises h with h_inv = 1 / h_scale
+  int tensor;
+  const float* a_tscale;  // FC1: x scale [1]
+  const float* b_tscale;  // weight scale per local expert [EL]
+  float h_scale, h_inv;
 };
 
 // Tile shape: BM rows x BN weight rows, K advancing BK per stage through an NSTAGE ring,
@@ -248,13 +254,13 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   if (bsf_mine) {
     const int blk = tid / nk128, ks = tid - blk * nk128;
     const int br = MODE == 1 ? (blk == 0 ? n0 / 128 : (g.I + n0) / 128) : min(n0 / 128 + blk, g.N / 128 - 1);
-    bsf_v = bsf_e[(long long)br * nk128 + ks];
+    bsf_v = g.tensor ? 127 : bsf_e[(long long)br * nk128 + ks];
   }
   __syncthreads();
   // activation scales of the tile rows in LDS as [row][k step]: moved by 4-byte DMA when a
   // row is whole dwords (nk128 % 4 == 0), else by byte loads
   const uint8_t* asf_gbase = MODE == 1 ? g.A_sf : g.A_sf + (long long)row_begin * nk128;
-  const bool asf_dma = (nk128 & 3) == 0 && ((BM * nk128) & 255) == 0;
+  const bool asf_dma = !g.tensor && (nk128 & 3) == 0 && ((BM * nk128) & 255) == 0;
   constexpr int kAsfDma = (BM * kMaxKSteps / 256 + NW - 1) / NW;  // 64-lane DMAs per wave, at most
   const int asf_n = BM * nk128 / 256;                               // 64-lane DMAs of the tile
   uint32_t asf_off[kAsfDma];
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   } else {
     for (int i = tid; i < nk128 * BM; i += C::NTHR) {
       const int r = i / nk128;
-      s_asf[i] = asf_gbase[(long long)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * nk128 + (i - r * nk128)];
+      s_asf[i] = g.tensor ? 127 : asf_gbase[(long long)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * nk128 + (i - r * nk128)];
     }
   }
 
@@ -501,6 +507,16 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
     else run(std::false_type{});
   }
 
+  if (g.tensor) {  // per-tensor scales: one factor for the whole tile
+    const float sc = (MODE == 1 ? g.a_tscale[0] : g.h_scale) * g.b_tscale[e];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int ct = 0; ct < C::NT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mi][ct][i] *= sc;
+  }
+
   if (MODE == 2) {
     // ---- FC2 epilogue (tokens are the MFMA's first operand: lane l of acc[mi][ct] holds
     //      rows 8*(i/4) + 4*kb + i%4 of row tile mi, column bcol(ct) + l%32): fp32 rows of Y2,
@@ -590,18 +606,26 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
       mx = mx > o ? mx : o;
     }
     const int sfb = ue8m0_for_amax(__uint_as_float(mx));
-    const float inv = inv_scale_of(sfb);
     stage_sf[r] = (uint8_t)sfb;
     uint8_t* hrow = stage_h + r * 128;
+    // block scales keep every value within +-448; the static per-tensor scale saturates
+    auto pack = [&](float inv, auto sat) {
+      auto v = [&](int c, int j) {
+        const float t = acc[mi][c][j] * inv;
+        return decltype(sat)::value ? __builtin_amdgcn_fmed3f(t, -448.f, 448.f) : t;
+      };
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(acc[mi][c][4 * q] * inv, acc[mi][c][4 * q + 1] * inv, 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(acc[mi][c][4 * q + 2] * inv, acc[mi][c][4 * q + 3] * inv, word, true);
-        const int col = wn * (128 / C::WN) + c * 32 + 8 * q + 4 * kb;  // multiple of 4
-        *reinterpret_cast<int*>(hrow + ((((col >> 4) ^ (r & 7)) << 4) | (col & 15))) = word;
-      }
+        for (int q = 0; q < 4; ++q) {
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(v(c, 4 * q), v(c, 4 * q + 1), 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(v(c, 4 * q + 2), v(c, 4 * q + 3), word, true);
+          const int col = wn * (128 / C::WN) + c * 32 + 8 * q + 4 * kb;  // multiple of 4
+          *reinterpret_cast<int*>(hrow + ((((col >> 4) ^ (r & 7)) << 4) | (col & 15))) = word;
+        }
+    };
+    if (g.tensor) pack(g.h_inv, std::true_type{});
+    else pack(inv_scale_of(sfb), std::false_type{});
   }
   __syncthreads();
   for (int q = tid; q < BM * 8; q += C::NTHR) {
@@ -609,7 +633,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
     if (r < rows) {
       *reinterpret_cast<uint4*>(g.h + (long long)(row_begin + r) * g.I + n0 + c * 16) =
           *reinterpret_cast<const uint4*>(stage_h + r * 128 + ((c ^ (r & 7)) << 4));
-      if (c == 0) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = stage_sf[r];
+      if (c == 0 && !g.tensor) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = stage_sf[r];
     }
   }
 }
@@ -677,6 +701,16 @@ static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_
   return launch_variant_w<MODE, 0>(a, variant, grid, s);
 }
 
+// per-tensor scaling: the scale tensors hold float32 values (x: one, weights: one per expert)
+static void set_tensor_scales(GemmArgs& a, const Shape& sh, const float* a_scale, const float* b_scale) {
+  a.tensor = sh.tensor ? 1 : 0;
+  if (!sh.tensor) return;
+  a.a_tscale = a_scale;
+  a.b_tscale = b_scale;
+  a.h_scale = sh.h_scale;
+  a.h_inv = 1.0f / sh.h_scale;
+}
+
 hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
                       const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
                       uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s) {
@@ -687,6 +721,7 @@ hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint
   a.b_estride = sh.wfmt != 1 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
   a.act = sh.act; a.clamp = sh.clamp; a.alpha = sh.alpha; a.bias = sh.bias;
+  set_tensor_scales(a, sh, reinterpret_cast<const float*>(x_sf), reinterpret_cast<const float*>(w1_sf));
   const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -702,6 +737,7 @@ hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint
   a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL;
   a.b_estride = sh.wfmt != 1 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
+  set_tensor_scales(a, sh, nullptr, reinterpret_cast<const float*>(w2_sf));
   const int bn = variant == 0 ? 128 : 256;
   a.n_tiles = (sh.H + bn - 1) / bn;
   const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;

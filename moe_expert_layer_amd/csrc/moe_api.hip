@@ -105,6 +105,14 @@ moe_status check_desc(const moe_layer_desc* d) {
       return fail(MOE_ERR_INVALID_DESC, "act_alpha / act_up_bias must be finite");
   }
   if (d->variant < -1 || d->variant > 2) return fail(MOE_ERR_INVALID_DESC, "variant %d unknown", d->variant);
+  if (d->scale_mode != MOE_SCALE_BLOCK && d->scale_mode != MOE_SCALE_TENSOR)
+    return fail(MOE_ERR_INVALID_DESC, "scale_mode %d unknown", d->scale_mode);
+  if (d->scale_mode == MOE_SCALE_TENSOR) {
+    if (d->weight_format == MOE_W_MXFP4_E2M1_B32)
+      return fail(MOE_ERR_INVALID_DESC, "per-tensor scaling needs FP8 weights");
+    if (!std::isfinite(d->h_scale) || !(d->h_scale > 0.f))
+      return fail(MOE_ERR_INVALID_DESC, "h_scale must be finite and > 0");
+  }
   if (!moe::gemm_supports(d->hidden, d->inter))
     return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d above the supported 8192", d->hidden, d->inter);
   if ((long long)d->num_tokens * d->hidden >= (1LL << 32))
@@ -148,6 +156,8 @@ moe::Shape shape_of(const moe_layer_desc& d) {
   moe::Shape s;
   s.T = d.num_tokens; s.H = d.hidden; s.I = d.inter; s.E = d.num_experts; s.e0 = d.local_begin;
   s.EL = d.num_local; s.k = d.topk; s.wfmt = d.weight_format; s.act = d.activation;
+  s.tensor = d.scale_mode == MOE_SCALE_TENSOR;
+  s.h_scale = s.tensor ? d.h_scale : 1.f;
   if (d.activation == MOE_ACT_SWIGLU_OAI) {
     s.clamp = d.act_clamp; s.alpha = d.act_alpha; s.bias = d.act_up_bias;
   } else {
@@ -219,6 +229,8 @@ moe_status moe_desc_defaults(moe_layer_desc* d) {
   d->act_alpha = 1.0f;
   d->act_up_bias = 0.0f;
   d->variant = -1;
+  d->scale_mode = MOE_SCALE_BLOCK;
+  d->h_scale = 1.0f;
   return ok();
 }
 
@@ -250,7 +262,9 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* d, const uint8_t* x, con
                                   uint8_t* h_sf, void* ws, size_t ws_bytes, void* stream) {
   if (moe_status st = check_desc(d)) return st;
   if (d->num_tokens == 0) return ok();
-  if (!x || !x_sf || !w1 || !w1_sf || !offsets || !r2s || !h || !h_sf) return fail(MOE_ERR_NULL, "a required pointer is NULL");
+  const bool tensor = d->scale_mode == MOE_SCALE_TENSOR;
+  if (!x || !x_sf || !w1 || !w1_sf || !offsets || !r2s || !h || (!h_sf && !tensor))
+    return fail(MOE_ERR_NULL, "a required pointer is NULL");
   if (misaligned(x, 16) || misaligned(w1, 16) || misaligned(h, 16) || misaligned(x_sf, 16) || misaligned(w1_sf, 16))
     return fail(MOE_ERR_MISALIGNED, "x / x_sf / w1 / w1_sf / h not 16-byte aligned");
   if (moe_status st = check_ws(d, ws, ws_bytes)) return st;
@@ -268,7 +282,8 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* d, const uint8_t* h, co
                                    void* stream) {
   if (moe_status st = check_desc(d)) return st;
   if (d->num_tokens == 0) return ok();
-  if (!h || !h_sf || !w2 || !w2_sf || !offsets || !r2s || !s2r || !w || !y)
+  const bool tensor = d->scale_mode == MOE_SCALE_TENSOR;
+  if (!h || (!h_sf && !tensor) || !w2 || !w2_sf || !offsets || !r2s || !s2r || !w || !y)
     return fail(MOE_ERR_NULL, "a required pointer is NULL");
   if (misaligned(h, 16) || misaligned(w2, 16) || misaligned(y, 16) || misaligned(h_sf, 16) || misaligned(w2_sf, 16))
     return fail(MOE_ERR_MISALIGNED, "h / h_sf / w2 / w2_sf / y not 16-byte aligned");
@@ -321,6 +336,8 @@ moe_status moe_quantize_act(const moe_layer_desc* d, const uint16_t* x_bf16, uin
                             void* stream) {
   if (moe_status st = check_desc(d)) return st;
   if (d->num_tokens == 0) return ok();
+  if (d->scale_mode == MOE_SCALE_TENSOR)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_quantize_act makes blockwise scales only");
   if (!x_bf16 || !x || !x_sf) return fail(MOE_ERR_NULL, "x_bf16/x/x_sf NULL");
   if (misaligned(x_bf16, 16) || misaligned(x, 16)) return fail(MOE_ERR_MISALIGNED, "x_bf16/x not 16-byte aligned");
   if (moe_status st = check_device()) return st;

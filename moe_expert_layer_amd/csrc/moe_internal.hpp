@@ -15,6 +15,8 @@ constexpr int kPermSmallBuckets = 257;  // ... and at most 256 local experts
 struct Shape {
   int T, H, I, E, e0, EL, k;
   int wfmt;  // 0 E4M3 block-128, 1 mxfp4, 2 E5M2 block-128
+  bool tensor = false;  // per-tensor float32 scales instead of UE8M0 blocks
+  float h_scale = 1.f;  // per-tensor: static scale of the intermediate
   int act;   // 0 swiglu, 1 oai
   float clamp, alpha, bias;
 };

@@ -29,7 +29,7 @@ from typing import Dict
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "workload", "generate", "shrink"]
+__all__ = ["Workload", "WORKLOADS", "workload", "generate", "shrink", "tensor_scaled"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -50,6 +50,8 @@ class Workload:
     routing: str  # "normal" | "zipf"
     zipf_s: float
     seed: int
+    scaling: str = "block"  # "block" (UE8M0 blocks) | "tensor" (one float32 scale per tensor)
+    h_scale: float = 1.0    # "tensor" only: static scale of the intermediate
 
     @property
     def rows_capacity(self) -> int:
@@ -86,6 +88,16 @@ def workload(name_or_index) -> Workload:
 def shrink(w: Workload, **changes) -> Workload:
     """Same recipe with some sizes replaced (used for small parity cases)."""
     return dataclasses.replace(w, **changes)
+
+
+def tensor_scaled(w: Workload, h_scale: float | None = None, **changes) -> Workload:
+    """The workload with per-tensor float32 scales.  The static intermediate scale is a
+    calibration from the input statistics alone: gate and up pre-activations have variance
+    about 0.02^2 * H (unit-variance activations against weights of deviation 0.02), and
+    16 of those variances map to the E4M3 maximum 448 (larger values saturate)."""
+    if h_scale is None:
+        h_scale = float(np.float32(16.0 * 0.02 ** 2 * w.hidden / 448.0))
+    return dataclasses.replace(w, scaling="tensor", h_scale=h_scale, **changes)
 
 
 # ---------------------------------------------------------------------------
@@ -127,6 +139,13 @@ def _quant_fp8_blocks(v: np.ndarray, br: int, bc: int, fmt: str = "e4m3"):
     scaled = (vp.reshape(nb, br, kk // bc, bc) * inv[:, None, :, None]).reshape(nb * br, kk)
     q = _to_fp8_bytes(scaled[:n], fmt)
     return q, sf
+
+
+def _quant_fp8_tensor(v: np.ndarray, fmt: str = "e4m3"):
+    """v float32 -> FP8 bytes and one float32 scale amax / (format maximum) (1.0 for all zeros)."""
+    amax = float(np.abs(v).max()) if v.size else 0.0
+    s = np.float32(amax / _FP8[fmt][1]) if amax > 0 else np.float32(1.0)
+    return _to_fp8_bytes(v / s, fmt), s
 
 
 def _quant_mxfp4(v: np.ndarray):
@@ -174,7 +193,16 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: 
         prior = (-w.zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)
         logits = (logits + prior[None, :]).astype(np.float32)
     xf = _bf16_round(rng(1).standard_normal((T, H), dtype=np.float32))
-    x, x_sf = _quant_fp8_blocks(xf, 1, 128)
+    if w.scaling not in ("block", "tensor"):
+        raise ValueError(f"unknown scaling {w.scaling}")
+    tensor = w.scaling == "tensor"
+    if tensor and w.weight_format == "mxfp4":
+        raise ValueError("per-tensor scaling needs FP8 weights")
+    if tensor:
+        x, xs = _quant_fp8_tensor(xf)
+        x_sf = np.array([xs], np.float32)
+    else:
+        x, x_sf = _quant_fp8_blocks(xf, 1, 128)
     out = {"logits": np.ascontiguousarray(logits), "x": x, "x_sf": x_sf}
     if with_bf16:
         out["x_bf16"] = (xf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
@@ -185,14 +213,21 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: 
     f8 = "e5m2" if w.weight_format == "fp8e5m2" else "e4m3"
     w1 = np.empty((EL, 2 * I, H if fp8 else H // 2), np.uint8)
     w1_sf = np.empty((EL, 2 * I // 128, H // 128) if fp8 else (EL, 2 * I, H // 32), np.uint8)
+    if tensor:
+        w1_sf = np.empty(EL, np.float32)
     w2 = np.empty((EL, H, I if fp8 else I // 2), np.uint8)
     w2_sf = np.empty((EL, H // 128, I // 128) if fp8 else (EL, H, I // 32), np.uint8)
+    if tensor:
+        w2_sf = np.empty(EL, np.float32)
 
     def one(e):
         for which, shape, dst, dsf in ((0, (2 * I, H), w1, w1_sf), (1, (H, I), w2, w2_sf)):
             a = rng(2 + 2 * e + which).standard_normal(shape, dtype=np.float32)
             a *= np.float32(0.02)
-            q, s = _quant_fp8_blocks(a, 128, 128, f8) if fp8 else _quant_mxfp4(a)
+            if tensor:
+                q, s = _quant_fp8_tensor(a, f8)
+            else:
+                q, s = _quant_fp8_blocks(a, 128, 128, f8) if fp8 else _quant_mxfp4(a)
             dst[e], dsf[e] = q, s
 
     with cf.ThreadPoolExecutor(max_workers=max(1, threads)) as ex:

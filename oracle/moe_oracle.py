@@ -14,6 +14,8 @@ one GPU's share of the experts, written from the pages' description of the fused
              against FP8 (E4M3 or E5M2) weights with 128x128 UE8M0 block scales (or MXFP4)
   activation SwiGLU, or parameterised OAI-SwiGLU (clamp, sigmoid alpha, up bias)
   requant    the intermediate back to FP8 E4M3 with one UE8M0 scale per 1x128 block
+             (per-tensor variant: float32 scales for x and each expert's weights, and a
+             static float32 scale for the intermediate, E4M3 codes saturated at 448)
   quantize   (input side) bf16 activations to FP8 E4M3 with the same 1x128 UE8M0 rule
   FC2        down projection of the requantised intermediate
   combine    top-k weighted sum of each token's local rows, back in token order
@@ -52,7 +54,7 @@ import numpy as np
 
 __all__ = [
     "decode_e4m3", "decode_e5m2", "decode_ue8m0", "decode_e2m1", "encode_e4m3_rne", "bf16_rne_bits",
-    "dequant_act", "dequant_weight", "route", "permute", "activation", "requant_1x128",
+    "dequant_act", "dequant_weight", "route", "permute", "activation", "requant_1x128", "requant_tensor",
     "expert_rows", "combine", "layer", "layer_tokens",
 ]
 
@@ -259,6 +261,13 @@ def requant_1x128(h32: np.ndarray):
     return codes, byte.astype(np.uint8)
 
 
+def requant_tensor(h32: np.ndarray, h_scale: float) -> np.ndarray:
+    """float32 rows -> E4M3 codes of h / h_scale (float64 quotient), saturated to +-448, round
+    to nearest even (the per-tensor variant's static-scale quantisation)."""
+    v = np.asarray(h32, dtype=np.float32).astype(np.float64) / float(np.float32(h_scale))
+    return encode_e4m3_rne(np.clip(v, -448.0, 448.0))
+
+
 def decode_bf16(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns -> float32 (the upper half of the float32 pattern; exact)."""
     b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
@@ -311,6 +320,20 @@ def expert_rows(d, inputs, e: int, tokens: np.ndarray):
     Returns (h codes [n, I], h scales [n, I/128], Y2 float64 [n, H]).
     """
     H, I, fmt = d.hidden, d.inter, d.weight_format
+    if getattr(d, "scaling", "block") == "tensor":
+        # per-tensor: every scale is one float32 (x: [1], weights: one per expert), the
+        # intermediate uses the descriptor's static h_scale; h_sf is not produced (zeros)
+        dec = decode_e4m3 if fmt == "fp8" else decode_e5m2
+        sc = lambda a: float(np.float32(a))
+        x = decode_e4m3(inputs["x"][tokens]) * sc(inputs["x_sf"][0])
+        w1 = dec(inputs["w1"][e]) * sc(inputs["w1_sf"][e])
+        gu = x @ w1.T
+        h = activation(gu[:, :I], gu[:, I:], d.activation, d.act_clamp, d.act_alpha, d.act_up_bias)
+        hq = requant_tensor(h.astype(np.float32), d.h_scale)
+        hs = np.zeros((hq.shape[0], I // 128), np.uint8)
+        hd = decode_e4m3(hq) * sc(d.h_scale)
+        w2 = dec(inputs["w2"][e]) * sc(inputs["w2_sf"][e])
+        return hq, hs, hd @ w2.T
     x = dequant_act(inputs["x"][tokens], inputs["x_sf"][tokens])
     w1 = dequant_weight(inputs["w1"][e], inputs["w1_sf"][e], fmt, 2 * I, H)
     gu = x @ w1.T

@@ -129,16 +129,34 @@ def topk_bruteforce(logits_row, k):
     return ids, ls
 
 
+def requant_tensor_row(h: np.ndarray, h_scale: float):
+    """float32 row -> E4M3 codes of h / h_scale (exact rational quotient, saturated at 448)."""
+    s = Fraction(float(np.float32(h_scale)))
+    out = []
+    for v in h:
+        q = Fraction(float(v)) / s
+        q = max(Fraction(-448), min(Fraction(448), q))
+        out.append(e4m3_nearest_code(q if q != 0 else math.copysign(0.0, float(v))))
+    return np.array(out, dtype=np.uint8)
+
+
 def layer_bruteforce(d, inputs):
     """Token-by-token dense evaluation: y[t] = sum_j w_tj * FFN_{e_tj}(x_t), float64."""
     T, H, I, k = d.tokens, d.hidden, d.inter, d.topk
+    tensor = getattr(d, "scaling", "block") == "tensor"
     xs = np.zeros((T, H))
     xv = decode_e4m3_torch(inputs["x"])
     for t in range(T):
         for c in range(H):
-            xs[t, c] = xv[t, c] * 2.0 ** (int(inputs["x_sf"][t, c // 128]) - 127)
-    w1 = [weight_dense(inputs["w1"][e], inputs["w1_sf"][e], d.weight_format, 2 * I, H) for e in range(d.num_local)]
-    w2 = [weight_dense(inputs["w2"][e], inputs["w2_sf"][e], d.weight_format, H, I) for e in range(d.num_local)]
+            s = float(inputs["x_sf"][0]) if tensor else 2.0 ** (int(inputs["x_sf"][t, c // 128]) - 127)
+            xs[t, c] = xv[t, c] * s
+    if tensor:
+        dec = decode_e4m3_torch if d.weight_format == "fp8" else decode_e5m2_torch
+        w1 = [dec(inputs["w1"][e]) * float(inputs["w1_sf"][e]) for e in range(d.num_local)]
+        w2 = [dec(inputs["w2"][e]) * float(inputs["w2_sf"][e]) for e in range(d.num_local)]
+    else:
+        w1 = [weight_dense(inputs["w1"][e], inputs["w1_sf"][e], d.weight_format, 2 * I, H) for e in range(d.num_local)]
+        w2 = [weight_dense(inputs["w2"][e], inputs["w2_sf"][e], d.weight_format, H, I) for e in range(d.num_local)]
     y = np.zeros((T, H))
     for t in range(T):
         ids, ls = topk_bruteforce(inputs["logits"][t], k)
@@ -155,8 +173,13 @@ def layer_bruteforce(d, inputs):
             u = np.array([sum(xs[t, c] * w1[le][I + n, c] for c in range(H)) for n in range(I)])
             h = np.array([act_scalar(g[n], u[n], d.activation, d.act_clamp, d.act_alpha, d.act_up_bias)
                           for n in range(I)], dtype=np.float32)
-            hq, hs = requant_row(h)
-            hd = np.array([decode_e4m3_torch(hq[n:n + 1])[0] * 2.0 ** (int(hs[n // 128]) - 127) for n in range(I)])
+            if tensor:
+                hq = requant_tensor_row(h, d.h_scale)
+                hd = np.array([decode_e4m3_torch(hq[n:n + 1])[0] * float(np.float32(d.h_scale)) for n in range(I)])
+            else:
+                hq, hs = requant_row(h)
+                hd = np.array([decode_e4m3_torch(hq[n:n + 1])[0] * 2.0 ** (int(hs[n // 128]) - 127)
+                               for n in range(I)])
             for m in range(H):
                 y[t, m] += wt * sum(hd[n] * w2[le][m, n] for n in range(I))
     return y

@@ -50,7 +50,8 @@ def run_layer(w, dev, variant=-1):
 
 
 def run_split(w, dev, variant=-1):
-    """The three-call path; also returns h / h_sf."""
+    """The three-call path; also returns h / h_sf (per-tensor scaling: h_sf is passed as NULL
+    and returned as zeros)."""
     d = B.desc_from_workload(w, variant)
     ws = B.alloc_workspace(d)
     T, k, EL, I = w.tokens, w.topk, w.num_local, w.inter
@@ -58,13 +59,15 @@ def run_split(w, dev, variant=-1):
     counts, offsets, r2s, s2r = i32(EL), i32(EL + 1), i32(T * k), i32(T * k)
     B.moe_route_permute(d, dev["logits"], ids, tw, counts, offsets, r2s, s2r, ws)
     h = torch.empty((T * k, I), dtype=torch.uint8, device="cuda")
-    h_sf = torch.empty((T * k, I // 128), dtype=torch.uint8, device="cuda")
+    tensor = getattr(w, "scaling", "block") == "tensor"
+    h_sf = None if tensor else torch.empty((T * k, I // 128), dtype=torch.uint8, device="cuda")
     B.moe_grouped_fc1_swiglu(d, dev["x"], dev["x_sf"], dev["w1"], dev["w1_sf"], offsets, r2s, h, h_sf, ws)
     y = torch.empty((T, w.hidden), dtype=torch.int16, device="cuda")
     B.moe_grouped_fc2_combine(d, h, h_sf, dev["w2"], dev["w2_sf"], offsets, r2s, s2r, tw, y, ws)
     torch.cuda.synchronize()
     R = int(offsets[-1].item())
-    return {"y_bf16": y.cpu().numpy().view(np.uint16), "h": h[:R].cpu().numpy(), "h_sf": h_sf[:R].cpu().numpy(),
+    hs = np.zeros((R, I // 128), np.uint8) if tensor else h_sf[:R].cpu().numpy()
+    return {"y_bf16": y.cpu().numpy().view(np.uint16), "h": h[:R].cpu().numpy(), "h_sf": hs,
             "R": R, "offsets": offsets.cpu().numpy(), "row_to_slot": r2s.cpu().numpy(),
             "slot_to_row": s2r.cpu().numpy(), "topk_ids": ids.cpu().numpy(), "topk_w": tw.cpu().numpy(),
             "counts": counts.cpu().numpy()}

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert B.status_str(0) == "MOE_OK" and B.status_str(5) == "MOE_ERR_WORKSPACE"
     assert B.status_str(99) == "MOE_STATUS_UNKNOWN"
 
@@ -49,6 +49,7 @@ def test_defaults_follow_standard_swiglu(L):
     assert L.moe_desc_defaults(ctypes.byref(d)) == 0
     assert d.activation == B.MOE_ACT_SWIGLU and d.weight_format == B.MOE_W_FP8_E4M3_B128
     assert math.isinf(d.act_clamp) and d.act_alpha == 1.0 and d.act_up_bias == 0.0 and d.variant == -1
+    assert d.scale_mode == B.MOE_SCALE_BLOCK and d.h_scale == 1.0
 
 
 @pytest.mark.parametrize("i", range(5))
@@ -63,7 +64,7 @@ def test_workspace_size_covers_capacity(L, i):
 @pytest.mark.parametrize("field,value", [("hidden", 100), ("inter", 0), ("num_experts", 0), ("num_experts", 2000),
                                          ("topk", 0), ("topk", 17), ("num_local", 0), ("local_begin", -1),
                                          ("num_tokens", -5), ("weight_format", 7), ("activation", 3),
-                                         ("variant", 5)])
+                                         ("variant", 5), ("scale_mode", 2)])
 def test_invalid_descriptor_rejected(L, field, value):
     d = B.desc_from_workload(synth.workload("tiny"))
     setattr(d, field, value)
@@ -139,3 +140,30 @@ def test_pack_scales_validation(L):
     assert L.moe_pack_scales(4, 4, None, P(0x2000), None) == B.MOE_ERR_NULL
     assert L.moe_unpack_scales(4, 4, P(0x2002), P(0x1000), None) == B.MOE_ERR_MISALIGNED
     assert L.moe_pack_scales(0, 4, None, None, None) == B.MOE_OK
+
+
+def test_per_tensor_scaling_validated(L):
+    n = ctypes.c_size_t(0)
+    d = B.desc_from_workload(synth.tensor_scaled(synth.workload("tiny")))
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_OK
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        d.h_scale = bad
+        assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_INVALID_DESC
+    d.h_scale = 0.5
+    d.weight_format = B.MOE_W_MXFP4_E2M1_B32
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_INVALID_DESC
+    d.weight_format = B.MOE_W_FP8_E5M2_B128
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_OK
+    # the input quantiser makes blockwise scales only
+    P = ctypes.c_void_p
+    assert L.moe_quantize_act(ctypes.byref(d), P(0x1000), P(0x2000), P(0x3000), None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_h_sf_optional_only_with_per_tensor_scaling(L):
+    P = ctypes.c_void_p
+    args = [P(0x10000)] * 6 + [P(0x20000), None]  # x, x_sf, w1, w1_sf, offsets, row_to_slot, h, h_sf
+    d = B.desc_from_workload(synth.workload("tiny"))
+    assert L.moe_grouped_fc1_swiglu(ctypes.byref(d), *args, P(0x100000), 16, None) == B.MOE_ERR_NULL
+    d = B.desc_from_workload(synth.tensor_scaled(synth.workload("tiny")))
+    # past the pointer checks: the undersized workspace is what is reported
+    assert L.moe_grouped_fc1_swiglu(ctypes.byref(d), *args, P(0x100000), 16, None) == B.MOE_ERR_WORKSPACE

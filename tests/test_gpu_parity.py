@@ -40,6 +40,12 @@ def _small_cases():
         # E5M2 weights (activations stay E4M3): MFMA weight-operand format 1
         ("e5m2_small", synth.shrink(oai, tokens=300, hidden=768, inter=384, num_experts=16, num_local=8, topk=4,
                                     weight_format="fp8e5m2", seed=15)),
+        # per-tensor float32 scales; the second case saturates about 4.5% of h at 448 * h_scale
+        ("tensor_oai", synth.tensor_scaled(synth.shrink(oai, tokens=600, hidden=1024, inter=384, num_experts=8,
+                                                        num_local=8, topk=2, seed=16))),
+        ("tensor_e5m2_sat", synth.tensor_scaled(synth.shrink(oai, tokens=200, hidden=512, inter=256, num_experts=16,
+                                                             local_begin=4, num_local=8, topk=4,
+                                                             weight_format="fp8e5m2", seed=17), h_scale=0.0015)),
         ("top1", synth.shrink(tiny, tokens=130, topk=1, seed=11)),
         ("k16_e1024", synth.shrink(tiny, tokens=40, num_experts=1024, local_begin=1000, num_local=24, topk=16,
                                    seed=12)),
@@ -78,7 +84,7 @@ def test_layer_parity_small(name, w):
 
 @pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("name", ["ragged_oai", "ragged_h384_share", "zipf_small", "mxfp4_small", "e5m2_small",
-                                  "k16_e1024"])
+                                  "tensor_oai", "k16_e1024"])
 def test_layer_parity_forced_variant(name, variant):
     w = dict(_small_cases())[name]
     G.say(f"[variant] {name} variant={variant}")
@@ -101,12 +107,14 @@ def test_run_twice_bit_identical():
     assert np.array_equal(a["y_bf16"], b["y_bf16"])
 
 
+@pytest.mark.parametrize("scaling", ["block", "tensor"])
 @pytest.mark.parametrize("fmt", ["fp8", "fp8e5m2"])
 @pytest.mark.parametrize("variant", [-1, 0, 1, 2])
-def test_exact_integer_layer_bit_exact(variant, fmt):
+def test_exact_integer_layer_bit_exact(variant, fmt, scaling):
     """Small-integer operands, unit scales, top-1, OAI with alpha 0: every partial sum is exact in
     fp32 (x, W2 in {-1, 0, 1}; W1 rows with at most 4 non-zeros so |g|, |u| <= 4 and h = g*u/2 is a
-    half-integer <= 8 that the requant reproduces exactly), so the GPU output equals the oracle bit for bit."""
+    half-integer <= 8 that the requant reproduces exactly), so the GPU output equals the oracle bit for bit.
+    With per-tensor scaling every scale is 1.0 (h_scale too)."""
     rng = np.random.default_rng(9)
     T, H, I, E = 200, 256, 256, 4
     w = synth.shrink(synth.workload("tiny"), tokens=T, hidden=H, inter=I, num_experts=E, num_local=E, topk=1,
@@ -127,6 +135,9 @@ def test_exact_integer_layer_bit_exact(variant, fmt):
            "x_sf": np.full((T, H // 128), 127, np.uint8), "w1": w1,
            "w1_sf": np.full((E, 2 * I // 128, H // 128), 127, np.uint8), "w2": pm1((E, H, I), 0.3, WONE, WMONE),
            "w2_sf": np.full((E, H // 128, I // 128), 127, np.uint8)}
+    if scaling == "tensor":
+        w = synth.tensor_scaled(w, h_scale=1.0)
+        inp.update(x_sf=np.ones(1, np.float32), w1_sf=np.ones(E, np.float32), w2_sf=np.ones(E, np.float32))
     ref = O.layer(w, inp)
     got = G.run_split(w, G.upload(inp), variant=variant)
     assert np.array_equal(got["h"], ref["h"]) and np.array_equal(got["h_sf"], ref["h_sf"])
