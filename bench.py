@@ -87,6 +87,7 @@ def main():
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--weights", choices=["fp8", "fp8e5m2", "mxfp4"], default=None,
                     help="replace the workload's weight format (FP8 E4M3, FP8 E5M2 or MXFP4)")
+    ap.add_argument("--shared", type=int, default=0, help="shared experts (every token, weight 1)")
     ap.add_argument("--scaling", choices=["block", "tensor"], default="block",
                     help="blockwise UE8M0 scales, or one float32 scale per tensor (FP8 weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -124,6 +125,8 @@ def main():
         w = synth.shrink(w, weight_format=args.weights, name=f"{w.name}/{args.weights}")
     if args.scaling == "tensor":
         w = synth.tensor_scaled(w, name=f"{w.name}/tensor")
+    if args.shared:
+        w = synth.shrink(w, num_shared=args.shared, name=f"{w.name}/shared{args.shared}")
     t0 = time.time()
     inp = synth.generate(w)
     print(f"[bench] generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -161,8 +164,9 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
 
     cnt = counts.cpu().numpy()
-    R = int(cnt.sum())
-    active = int((cnt > 0).sum())
+    S = w.num_shared
+    R = int(cnt.sum()) + S * T           # routed rows, then the shared experts' T rows each
+    active = int((cnt > 0).sum()) + S    # experts whose weights are read
     alg = algorithmic(w, R, active, cnt)
 
     # dominant kernel: FC1 grouped GEMM (fused activation + requant), timed alone on the same stream
@@ -171,8 +175,8 @@ def main():
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
     B.moe_route_permute(d, dev["logits"], ids, tw, counts, offsets, r2s, s2r, ws, stream=stream)
-    h = torch.empty((T * k, w.inter), dtype=torch.uint8, device="cuda")
-    h_sf = torch.empty((T * k, w.inter // 128), dtype=torch.uint8, device="cuda")
+    h = torch.empty((T * (k + S), w.inter), dtype=torch.uint8, device="cuda")
+    h_sf = torch.empty((T * (k + S), w.inter // 128), dtype=torch.uint8, device="cuda")
     for i in range(3):
         w1, w1s, _, _ = wsets[i % len(wsets)]
         B.moe_grouped_fc1_swiglu(d, dev["x"], dev["x_sf"], w1, w1s, offsets, r2s, h, h_sf, ws, stream=stream)
@@ -233,7 +237,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "inter": w.inter,
                    "experts": w.num_experts, "local_experts": EL, "topk": k, "activation": w.activation,
-                   "weight_format": w.weight_format, "scaling": w.scaling, "rows": R, "active_experts": active,
+                   "weight_format": w.weight_format, "scaling": w.scaling, "shared_experts": S, "rows": R, "active_experts": active,
                    "parallelism": "one GPU's expert share", "weight_copies": len(wsets)},
         "tflops": round(tflops, 2), "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),

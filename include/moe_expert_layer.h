@@ -41,8 +41,9 @@
  *       offsets     int32 [E_loc+1] exclusive scan of counts; offsets[E_loc] = R
  *       row_to_slot int32 [T*k]  rows [0, R) hold slot ids s = t*k + j, rest -1
  *       slot_to_row int32 [T*k]  row of slot s, or -1 when expert ids[s] is not local
- *       h           E4M3 bytes [T*k, I] (rows [0, R) written), h_sf UE8M0 [T*k, I/128]
- *       y           bfloat16 bits [T, H]; tokens with no local slot get +0
+ *       h           E4M3 bytes [T*k + S*T, I] (rows [0, R + S*T) written), h_sf UE8M0
+ *                   [T*k + S*T, I/128]; S = num_shared (0 by default)
+ *       y           bfloat16 bits [T, H]; with S = 0, tokens with no local slot get +0
  *   - Requant rule: per 1x128 block, scale 2^e with the smallest integer e such that
  *     448 * 2^e >= amax (byte 127 for an all-zero block), codes = E4M3 round to
  *     nearest even of h * 2^-e.
@@ -55,6 +56,15 @@
  *                   h_scale (> 0, finite) is the static scale in the descriptor and
  *                   h_sf is neither read nor written (it may be NULL)
  *     Non-finite or non-positive tensor scales give unspecified results.
+ *   - Shared experts (num_shared = S > 0; the pages list shared-expert builds of the
+ *     kernel, "Sync upstream through PR #441", Validation): S more experts that every token
+ *     passes through with weight 1.  Their weights follow the routed local experts in
+ *     w1/w1_sf/w2/w2_sf, which then hold E_loc + S experts (per-tensor scales: E_loc + S
+ *     floats).  Their rows follow the routed rows: shared expert s owns h rows
+ *     [R + s*T, R + (s+1)*T), row R + s*T + t being token t, so h and h_sf hold
+ *     T*k + S*T rows.  y[t] adds them after the routed slots, in order s = 0..S-1, before
+ *     the single bf16 rounding.  counts, offsets, row_to_slot and slot_to_row describe the
+ *     routed rows only.
  *   - Logits must be finite; non-finite logits give unspecified routing.
  *   - Validation happens on the host before any launch; on error nothing is
  *     launched and a moe_status is returned (moe_last_error() has details).  A
@@ -67,7 +77,7 @@
  *     16-byte aligned, the workspace 256-byte aligned (MOE_ERR_MISALIGNED otherwise).
  *   - Limits: H and I multiples of 128 and at most 8192 (MOE_ERR_UNSUPPORTED above);
  *     1 <= E_loc <= E_tot <= 1024;
- *     1 <= k <= min(E_tot, 16); T*k < 2^31; x smaller than 4 GiB (T*H < 2^32,
+ *     1 <= k <= min(E_tot, 16); 0 <= S <= 4; T*(k + S) < 2^31; x smaller than 4 GiB (T*H < 2^32,
  *     MOE_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MOE_EXPERT_LAYER_H_
@@ -120,6 +130,7 @@ typedef struct {
                              2 = 32-row tiles */
   int32_t scale_mode;     /* moe_scale; default MOE_SCALE_BLOCK */
   float h_scale;          /* MOE_SCALE_TENSOR only: static scale of the intermediate h */
+  int32_t num_shared;     /* S in [0, 4]: shared experts applied to every token with weight 1 */
 } moe_layer_desc;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION at build time). */
@@ -148,7 +159,8 @@ moe_status moe_route_permute(const moe_layer_desc* desc, const float* logits, in
                              void* stream);
 
 /* FC1 + activation + 1x128 requant for every row of every local expert.
- * Reads x/x_sf rows of token row_to_slot[r] / k, writes h/h_sf rows [0, R). */
+ * Reads x/x_sf rows of token row_to_slot[r] / k (shared expert rows: every token in
+ * order), writes h/h_sf rows [0, R + S*T). */
 moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* desc, const uint8_t* x, const uint8_t* x_sf,
                                   const uint8_t* w1, const uint8_t* w1_sf, const int32_t* offsets,
                                   const int32_t* row_to_slot, uint8_t* h, uint8_t* h_sf,
@@ -156,7 +168,8 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* desc, const uint8_t* x, 
 
 /* FC2 + top-k weighted combine into y (bf16 bits, [T, H]).  The fp32 FC2 rows are
  * kept in the workspace; the sum over a token's local slots runs in slot order
- * j = 0..k-1 in fp32 and is rounded once to bf16. */
+ * j = 0..k-1 in fp32, then adds the shared experts' rows (weight 1), and is rounded
+ * once to bf16.  Reads h/h_sf rows [0, R + S*T). */
 moe_status moe_grouped_fc2_combine(const moe_layer_desc* desc, const uint8_t* h, const uint8_t* h_sf,
                                    const uint8_t* w2, const uint8_t* w2_sf, const int32_t* offsets,
                                    const int32_t* row_to_slot, const int32_t* slot_to_row,

@@ -32,6 +32,7 @@ class MoeLayerDesc(ctypes.Structure):
         ("topk", ctypes.c_int32), ("weight_format", ctypes.c_int32), ("activation", ctypes.c_int32),
         ("act_clamp", ctypes.c_float), ("act_alpha", ctypes.c_float), ("act_up_bias", ctypes.c_float),
         ("variant", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("h_scale", ctypes.c_float),
+        ("num_shared", ctypes.c_int32),
     ]
 
 
@@ -92,7 +93,7 @@ def make_desc(num_tokens: int, hidden: int, inter: int, num_experts: int, topk: 
               num_local: Optional[int] = None, weight_format: str = "fp8", activation: str = "swiglu",
               activation_clamp: Optional[float] = None, activation_alpha: float = 1.0,
               activation_up_bias: float = 0.0, variant: int = -1, scaling: str = "block",
-              h_scale: float = 1.0) -> MoeLayerDesc:
+              h_scale: float = 1.0, num_shared: int = 0) -> MoeLayerDesc:
     """Descriptor with the pages' keyword names (activation, activation_clamp/alpha/up_bias)."""
     d = MoeLayerDesc()
     _check(lib().moe_desc_defaults(ctypes.byref(d)))
@@ -107,13 +108,14 @@ def make_desc(num_tokens: int, hidden: int, inter: int, num_experts: int, topk: 
     d.variant = variant
     d.scale_mode = SCALINGS[scaling]
     d.h_scale = h_scale
+    d.num_shared = num_shared
     return d
 
 
 def desc_from_workload(w, variant: int = -1) -> MoeLayerDesc:
     return make_desc(w.tokens, w.hidden, w.inter, w.num_experts, w.topk, w.local_begin, w.num_local,
                      w.weight_format, w.activation, w.act_clamp, w.act_alpha, w.act_up_bias, variant,
-                     getattr(w, "scaling", "block"), getattr(w, "h_scale", 1.0))
+                     getattr(w, "scaling", "block"), getattr(w, "h_scale", 1.0), getattr(w, "num_shared", 0))
 
 
 def moe_workspace_size(desc: MoeLayerDesc) -> int:

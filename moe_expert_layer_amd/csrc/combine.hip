@@ -1,8 +1,9 @@
 // Top-k weighted combine back into token order, without atomics.
 //
-// y[t] = bf16( sum over local slots j = 0..k-1, in slot order, of w[t, j] * Y2[row(t, j)] )
-// accumulated in fp32 from 0 and rounded once to bfloat16; tokens with no local slot
-// get +0.  Sources: "Pull Style Cutedsl Megakernel" (Layout: the top-k reduce after
+// y[t] = bf16( sum over local slots j = 0..k-1, in slot order, of w[t, j] * Y2[row(t, j)]
+//             + sum over shared experts s = 0..S-1 of Y2[R + s T + t] )
+// accumulated in fp32 from 0 and rounded once to bfloat16; without shared experts, tokens
+// with no local slot get +0.  Sources: "Pull Style Cutedsl Megakernel" (Layout: the top-k reduce after
 // the fused FC1/FC2 schedule) and "Optimize sm100 version with token-aware BM240
 // tiling, native UE8M0, and direct combine" (description: combine into token order).
 // Every output element is written by exactly one thread, so the result does not depend
@@ -27,10 +28,12 @@ __device__ __forceinline__ float4 ld_stream(const float* p) {
 // batches of four whose row loads are all issued before the in-order accumulation.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y2, const int32_t* __restrict__ s2r,
                                                       const float* __restrict__ w, int T, int H, int k,
+                                                      const int32_t* __restrict__ r_total, int S,
                                                       uint16_t* __restrict__ y) {
   const int c0 = blockIdx.x * 2048 + threadIdx.x * 4;
   if (c0 >= H) return;
   const bool two = c0 + 1024 < H;
+  const int R = S > 0 ? *r_total : 0;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
     float acc[8];
 #pragma unroll
@@ -69,6 +72,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         }
       }
     }
+    for (int s = 0; s < S; ++s) {  // shared experts, weight 1
+      const float* src = y2 + ((long long)R + (long long)s * T + t) * H + c0;
+      const float4 a = ld_stream(src);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      if (two) {
+        const float4 b = ld_stream(src + 1024);
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      }
+    }
     uint16_t* dst = y + (long long)t * H + c0;
     *reinterpret_cast<uint2*>(dst) =
         make_uint2((uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16),
@@ -81,9 +93,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_combine(const float* y2, const int32_t* slot_to_row, const float* topk_w, int T, int H, int k,
-                          uint16_t* y, hipStream_t s) {
+                          const int32_t* r_total, int S, uint16_t* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  combine_kernel<<<dim3((H + 2047) / 2048, T < 65535 ? T : 65535), 256, 0, s>>>(y2, slot_to_row, topk_w, T, H, k, y);
+  combine_kernel<<<dim3((H + 2047) / 2048, T < 65535 ? T : 65535), 256, 0, s>>>(y2, slot_to_row, topk_w, T, H, k,
+                                                                                r_total, S, y);
   return hipGetLastError();
 }
 

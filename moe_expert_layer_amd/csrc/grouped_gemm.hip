@@ -5,6 +5,8 @@
 //        W1 FP8 E4M3 with 128x128 UE8M0 scales or MXFP4 with 1x32 UE8M0 scales)
 //      then SwiGLU / OAI-SwiGLU and the 1x128 requant to E4M3 + UE8M0 (fused epilogue).
 // FC2: Y2[r, m] = h_r . W2[e, m]  (fp32 rows kept for the combine).
+// Shared experts (applied to every token) follow the routed local experts: shared expert s
+// owns rows [R + s T, R + (s + 1) T), row R + s T + t being token t.
 //
 // Sources: "fix(sm90): support parameterized SwiGLU in FP8 MegaMoE" (Summary: the two
 // activation formulas, applied in the FC1 epilogue); "Optimize sm100 version with
@@ -68,7 +70,9 @@ struct GemmArgs {
   int N;                 // weight rows per expert (2I for FC1, H for FC2)
   int I;                 // intermediate size (FC1 epilogue)
   int k;                 // top-k (FC1 row -> token)
-  int EL;
+  int EL;                // routed local experts; shared experts EL .. EL + S - 1 follow them
+  int S;                 // shared experts: each has the T rows [offsets[EL] + s T, + T), one per token
+  int T;
   int n_tiles;
   int act;
   float clamp, alpha, bias;
@@ -194,12 +198,13 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   if (plan == nullptr) {
     int* s_plan = reinterpret_cast<int*>(ring);  // [EL + 1]
     int* s_wsum = s_plan + kMaxExperts + 8;      // [NW]
-    const int t = threadIdx.x, n = g.EL + 1, per = (n + C::NTHR - 1) / C::NTHR, beg = t * per;
+    const int t = threadIdx.x, n = g.EL + g.S + 1, per = (n + C::NTHR - 1) / C::NTHR, beg = t * per;
     int sum = 0;
     for (int j = 0; j < per; ++j) {
       const int ee = beg + j;
       if (ee < n) s_plan[ee] = sum;
       if (ee < g.EL) sum += (g.offsets[ee + 1] - g.offsets[ee] + BM - 1) / BM;
+      else if (ee < n - 1) sum += (g.T + BM - 1) / BM;
     }
     const int inc = wave_inclusive_scan(sum);
     if ((t & 63) == 63) s_wsum[t >> 6] = inc;
@@ -211,7 +216,8 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
     __syncthreads();
     plan = s_plan;
   }
-  const int total = plan[g.EL] * g.n_tiles;
+  const int NE = g.EL + g.S;  // experts with rows: routed, then shared
+  const int total = plan[NE] * g.n_tiles;
   const int bid = blockIdx.x;
   if (bid >= total) return;
   int L;  // XCD-aware order: dispatch is round-robin over 8 XCDs; each XCD gets a contiguous range
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
     const int x = bid & 7, p = bid >> 3, q = total >> 3, r = total & 7;
     L = x * q + (x < r ? x : r) + p;
   }
-  const int e = find_expert(plan, g.EL, L / g.n_tiles);
+  const int e = find_expert(plan, NE, L / g.n_tiles);
   const int mt_e = plan[e + 1] - plan[e];
   const int li = L - plan[e] * g.n_tiles;
   const int gn = g.n_tiles < kGroupN ? g.n_tiles : kGroupN;
@@ -228,8 +234,12 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   const int idx = li - grp * gn * mt_e;
   const int m_tile = idx / gsz;
   const int n_tile = grp * gn + idx % gsz;
-  const int row_begin = g.offsets[e] + m_tile * BM;
-  const int rows = min(BM, g.offsets[e + 1] - row_begin);
+  // rows of expert e: routed experts from the offsets, shared expert s = e - EL after them
+  const bool shared = e >= g.EL;
+  const int seg_begin = shared ? g.offsets[g.EL] + (e - g.EL) * g.T : g.offsets[e];
+  const int seg_end = shared ? seg_begin + g.T : g.offsets[e + 1];
+  const int row_begin = seg_begin + m_tile * BM;
+  const int rows = min(BM, seg_end - row_begin);
 
   // the wave index is made scalar for the 256-row tiles (fewer registers there); the 128-row
   // tiles, whose row-tile skipping switches on it, allocate fewer with it left in a VGPR
@@ -240,11 +250,11 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   const int nk128 = g.K / 128;   // scale steps
   const int n0 = MODE == 1 ? n_tile * 128 : n_tile * BN;
 
-  // ---- tile rows: the token (FC1) or h row (FC2) of each tile row; rows past the expert's
-  //      last row repeat the first one ----
+  // ---- tile rows: the token (FC1; row i of a shared expert is token i) or h row (FC2) of
+  //      each tile row; rows past the expert's last row repeat the first one ----
   for (int i = tid; i < BM; i += C::NTHR) {
     const int r = i < rows ? i : 0;
-    s_tok[i] = MODE == 1 ? g.row_to_slot[row_begin + r] / g.k : row_begin + r;
+    s_tok[i] = MODE == 2 ? row_begin + r : shared ? row_begin + r - seg_begin : g.row_to_slot[row_begin + r] / g.k;
   }
   // FP8 weight scales of the tile's two 128-row blocks (FC1: gate n0/128 and up (I+n0)/128;
   // FC2: n0/128 and n0/128 + 1, clamped), loaded now and written to LDS after the DMA issue
@@ -648,10 +658,11 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
 //            the activation rows are a small part of each stage.
 int gemm_block_m(int variant) { return variant == 1 ? 256 : variant == 2 ? 32 : 128; }
 
-size_t gemm_max_mtiles(int rows_cap, int EL, int variant) {
+size_t gemm_max_mtiles(int rows_cap, int EL, int variant, int T, int S) {
   const int bm = gemm_block_m(variant);
-  // sum_e ceil(c_e / bm) <= (R + EL * (bm - 1)) / bm with R <= rows_cap
-  return ((size_t)rows_cap + (size_t)EL * (bm - 1)) / bm;
+  // sum_e ceil(c_e / bm) <= (R + EL * (bm - 1)) / bm with R <= rows_cap, plus the shared
+  // experts' ceil(T / bm) each
+  return ((size_t)rows_cap + (size_t)EL * (bm - 1)) / bm + (size_t)S * (((size_t)T + bm - 1) / bm);
 }
 
 bool gemm_supports(int H, int I) { return H / 128 <= kMaxKSteps && I / 128 <= kMaxKSteps; }
@@ -716,13 +727,14 @@ hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint
                       uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s) {
   GemmArgs a{};
   a.A = x; a.A_sf = x_sf; a.row_to_slot = row_to_slot; a.B = w1; a.B_sf = w1_sf;
-  a.offsets = offsets; a.plan = plan_ready ? plan : nullptr; a.h = h; a.h_sf = h_sf;
-  a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.n_tiles = sh.I / 128;
+  // the permute's tile plan covers the routed experts only
+  a.offsets = offsets; a.plan = plan_ready && sh.S == 0 ? plan : nullptr; a.h = h; a.h_sf = h_sf;
+  a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.S = sh.S; a.T = sh.T; a.n_tiles = sh.I / 128;
   a.b_estride = sh.wfmt != 1 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
   a.act = sh.act; a.clamp = sh.clamp; a.alpha = sh.alpha; a.bias = sh.bias;
   set_tensor_scales(a, sh, reinterpret_cast<const float*>(x_sf), reinterpret_cast<const float*>(w1_sf));
-  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
+  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, sh.S) * (size_t)a.n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   return launch_variant<1>(a, sh.wfmt, variant, grid, s);
@@ -732,15 +744,16 @@ hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint
                       const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, bool plan_ready,
                       hipStream_t s) {
   GemmArgs a{};
-  a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets; a.plan = plan_ready ? plan : nullptr;
+  a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets;
+  a.plan = plan_ready && sh.S == 0 ? plan : nullptr;
   a.y2 = y2;
-  a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL;
+  a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.S = sh.S; a.T = sh.T;
   a.b_estride = sh.wfmt != 1 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
   set_tensor_scales(a, sh, nullptr, reinterpret_cast<const float*>(w2_sf));
   const int bn = variant == 0 ? 128 : 256;
   a.n_tiles = (sh.H + bn - 1) / bn;
-  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant) * (size_t)a.n_tiles;
+  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, sh.S) * (size_t)a.n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   return launch_variant<2>(a, sh.wfmt, variant, grid, s);

@@ -70,9 +70,10 @@ Layout make_layout(const moe_layer_desc& d) {
   L.chunk_cnt = take(nchunks * NB * 4);
   L.chunk_base = take(nchunks * NB * 4);
   L.plan1 = take(NB * 4);
-  L.h = take(cap * (size_t)d.inter);
-  L.h_sf = take(cap * (size_t)(d.inter / 128));
-  L.y2 = take(cap * (size_t)d.hidden * 4);
+  const size_t hrows = cap + (size_t)d.num_shared * d.num_tokens;  // routed rows, then shared experts' rows
+  L.h = take(hrows * (size_t)d.inter);
+  L.h_sf = take(hrows * (size_t)(d.inter / 128));
+  L.y2 = take(hrows * (size_t)d.hidden * 4);
   L.total = at;
   return L;
 }
@@ -105,6 +106,10 @@ moe_status check_desc(const moe_layer_desc* d) {
       return fail(MOE_ERR_INVALID_DESC, "act_alpha / act_up_bias must be finite");
   }
   if (d->variant < -1 || d->variant > 2) return fail(MOE_ERR_INVALID_DESC, "variant %d unknown", d->variant);
+  if (d->num_shared < 0 || d->num_shared > moe::kMaxShared)
+    return fail(MOE_ERR_INVALID_DESC, "num_shared %d outside [0, %d]", d->num_shared, moe::kMaxShared);
+  if ((long long)d->num_tokens * (d->topk + d->num_shared) >= (1LL << 31))
+    return fail(MOE_ERR_INVALID_DESC, "num_tokens * (topk + num_shared) must be < 2^31");
   if (d->scale_mode != MOE_SCALE_BLOCK && d->scale_mode != MOE_SCALE_TENSOR)
     return fail(MOE_ERR_INVALID_DESC, "scale_mode %d unknown", d->scale_mode);
   if (d->scale_mode == MOE_SCALE_TENSOR) {
@@ -156,6 +161,7 @@ moe::Shape shape_of(const moe_layer_desc& d) {
   moe::Shape s;
   s.T = d.num_tokens; s.H = d.hidden; s.I = d.inter; s.E = d.num_experts; s.e0 = d.local_begin;
   s.EL = d.num_local; s.k = d.topk; s.wfmt = d.weight_format; s.act = d.activation;
+  s.S = d.num_shared;
   s.tensor = d.scale_mode == MOE_SCALE_TENSOR;
   s.h_scale = s.tensor ? d.h_scale : 1.f;
   if (d.activation == MOE_ACT_SWIGLU_OAI) {
@@ -294,7 +300,8 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* d, const uint8_t* h, co
   float* y2 = region<float>(ws, L.y2);
   MOE_TRY_HIP(moe::launch_fc2(sh, pick_variant(*d), h, h_sf, w2, w2_sf, offsets, y2, nullptr,
                               false, (hipStream_t)stream));
-  MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, y, (hipStream_t)stream));
+  MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, offsets + d->num_local,
+                                  d->num_shared, y, (hipStream_t)stream));
   return ok();
 }
 
@@ -328,7 +335,8 @@ moe_status moe_layer(const moe_layer_desc* d, const float* logits, const uint8_t
   MOE_TRY_HIP(moe::launch_fc1(sh, variant, x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf, region<int32_t>(ws, L.plan1),
                               true, s));
   MOE_TRY_HIP(moe::launch_fc2(sh, variant, h, h_sf, w2, w2_sf, offsets, y2, region<int32_t>(ws, L.plan1), true, s));
-  MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, y, s));
+  MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, offsets + d->num_local,
+                                  d->num_shared, y, s));
   return ok();
 }
 

@@ -8,6 +8,7 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 16;
+constexpr int kMaxShared = 4;  // shared experts per layer
 constexpr int kPermChunk = 4096;  // slots per permute workgroup
 constexpr int kPermSmallSlots = 16384;  // at most this many slots: one-workgroup permute
 constexpr int kPermSmallBuckets = 257;  // ... and at most 256 local experts
@@ -15,6 +16,7 @@ constexpr int kPermSmallBuckets = 257;  // ... and at most 256 local experts
 struct Shape {
   int T, H, I, E, e0, EL, k;
   int wfmt;  // 0 E4M3 block-128, 1 mxfp4, 2 E5M2 block-128
+  int S = 0;            // shared experts (weights after the EL routed ones)
   bool tensor = false;  // per-tensor float32 scales instead of UE8M0 blocks
   float h_scale = 1.f;  // per-tensor: static scale of the intermediate
   int act;   // 0 swiglu, 1 oai
@@ -34,7 +36,7 @@ hipError_t launch_permute(const int32_t* ids, int nslots, int e0, int EL, int32_
 int gemm_block_m(int variant);
 // largest contraction the GEMM kernels stage scales for (K / 128 <= 64)
 bool gemm_supports(int H, int I);
-size_t gemm_max_mtiles(int rows_cap, int EL, int variant);
+size_t gemm_max_mtiles(int rows_cap, int EL, int variant, int T, int S);
 // plan_ready: `plan` holds the tile plan of these offsets for this variant's tile rows (written
 // by launch_permute); otherwise `plan` is ignored and every GEMM workgroup derives the plan
 // from `offsets` in its prologue.
@@ -53,7 +55,8 @@ hipError_t launch_pack_scales(const uint8_t* sf, int M, int G, int32_t* packed, 
 hipError_t launch_unpack_scales(const int32_t* packed, int M, int G, uint8_t* sf, hipStream_t s);
 
 // combine --------------------------------------------------------------------
+// r_total: device pointer to R (offsets[EL]); shared expert s's rows start at R + s T
 hipError_t launch_combine(const float* y2, const int32_t* slot_to_row, const float* topk_w, int T, int H, int k,
-                          uint16_t* y, hipStream_t s);
+                          const int32_t* r_total, int S, uint16_t* y, hipStream_t s);
 
 }  // namespace moe

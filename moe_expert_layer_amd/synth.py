@@ -52,10 +52,11 @@ class Workload:
     seed: int
     scaling: str = "block"  # "block" (UE8M0 blocks) | "tensor" (one float32 scale per tensor)
     h_scale: float = 1.0    # "tensor" only: static scale of the intermediate
+    num_shared: int = 0     # shared experts (every token, weight 1), stored after the local ones
 
     @property
     def rows_capacity(self) -> int:
-        return self.tokens * self.topk
+        return self.tokens * (self.topk + self.num_shared)
 
 
 _INF = float("inf")
@@ -180,14 +181,15 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: 
     ``with_bf16`` also returns the bf16 activations before their quantisation, as bit
     patterns ``x_bf16`` [T, H] uint16.
 
-    Seed tree: SeedSequence(seed).spawn(2 + 2 * E_loc) gives the streams for the logits,
-    the activations, then W1 and W2 of each local expert in order; experts are drawn in
-    a thread pool, which does not change the values.
+    Seed tree: SeedSequence(seed).spawn(2 + 2 * (E_loc + S)) gives the streams for the
+    logits, the activations, then W1 and W2 of each local expert in order, the S shared
+    experts last; experts are drawn in a thread pool, which does not change the values.
     """
     seed = w.seed if seed is None else seed
-    kids = np.random.SeedSequence(seed).spawn(2 + 2 * w.num_local)
+    kids = np.random.SeedSequence(seed).spawn(2 + 2 * (w.num_local + w.num_shared))
     rng = lambda i: np.random.Generator(np.random.PCG64(kids[i]))
-    T, H, I, E, EL = w.tokens, w.hidden, w.inter, w.num_experts, w.num_local
+    T, H, I, E = w.tokens, w.hidden, w.inter, w.num_experts
+    EL = w.num_local + w.num_shared  # weight sets: routed local experts, then shared ones
     logits = rng(0).standard_normal((T, E), dtype=np.float32)
     if w.routing == "zipf":
         prior = (-w.zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)

@@ -19,6 +19,8 @@ one GPU's share of the experts, written from the pages' description of the fused
   quantize   (input side) bf16 activations to FP8 E4M3 with the same 1x128 UE8M0 rule
   FC2        down projection of the requantised intermediate
   combine    top-k weighted sum of each token's local rows, back in token order
+  shared     (variant) S shared experts that every token passes through with weight 1,
+             added after the routed slots
 
 Sources (pages of the study, cited by title and section):
   * "fix(sm90): support parameterized SwiGLU in FP8 MegaMoE" (DeepGEMM PR #445),
@@ -366,18 +368,22 @@ def layer_tokens(d, inputs, tokens=None):
     Routing and grouping always cover every token (they define the row numbering);
     FC1/FC2 are evaluated only for the rows of the requested tokens.  ``h``/``h_sf``
     are indexed by row and hold valid data only for evaluated rows (``h_valid``).
+    Shared experts (``num_shared`` = S, weights at indices E_loc .. E_loc + S - 1) own
+    rows R + s*T + t after the routed rows and join every token with weight 1.
     """
     T, k, E_loc = d.tokens, d.topk, d.num_local
+    S = getattr(d, "num_shared", 0)
     ids, w = route(inputs["logits"], k)
     counts, offsets, r2s, s2r = permute(ids, d.local_begin, E_loc)
     R = int(offsets[-1])
+    NR = R + S * T  # rows: routed, then the shared experts' (token order)
     toks = np.arange(T) if tokens is None else np.asarray(sorted(set(int(t) for t in tokens)), dtype=np.int64)
     want = np.zeros(T, dtype=bool)
     want[toks] = True
-    y2 = np.zeros((max(R, 1), d.hidden), dtype=np.float64)
-    h = np.zeros((max(R, 1), d.inter), dtype=np.uint8)
-    h_sf = np.zeros((max(R, 1), d.inter // 128), dtype=np.uint8)
-    h_valid = np.zeros(max(R, 1), dtype=bool)
+    y2 = np.zeros((max(NR, 1), d.hidden), dtype=np.float64)
+    h = np.zeros((max(NR, 1), d.inter), dtype=np.uint8)
+    h_sf = np.zeros((max(NR, 1), d.inter // 128), dtype=np.uint8)
+    h_valid = np.zeros(max(NR, 1), dtype=bool)
     for e in range(E_loc):
         rows = np.arange(offsets[e], offsets[e + 1])
         if rows.size == 0:
@@ -390,10 +396,19 @@ def layer_tokens(d, inputs, tokens=None):
         hq, hs, yy = expert_rows(d, inputs, e, rtok)
         h[rows], h_sf[rows], y2[rows] = hq, hs, yy
         h_valid[rows] = True
+    for s in range(S):
+        if toks.size == 0:
+            break
+        rows = R + s * T + toks
+        hq, hs, yy = expert_rows(d, inputs, E_loc + s, toks)
+        h[rows], h_sf[rows], y2[rows] = hq, hs, yy
+        h_valid[rows] = True
     y64 = combine(w, s2r, y2, toks, k)
+    for s in range(S):  # after the routed slots, weight 1
+        y64 = y64 + y2[R + s * T + toks]
     return {
         "topk_ids": ids, "topk_w": w, "counts": counts, "offsets": offsets,
         "row_to_slot": r2s, "slot_to_row": s2r, "R": R,
-        "h": h[:R], "h_sf": h_sf[:R], "h_valid": h_valid[:R],
+        "h": h[:NR], "h_sf": h_sf[:NR], "h_valid": h_valid[:NR],
         "tokens": toks, "y64": y64, "y_bf16": bf16_rne_bits(y64),
     }

@@ -144,6 +144,8 @@ def layer_bruteforce(d, inputs):
     """Token-by-token dense evaluation: y[t] = sum_j w_tj * FFN_{e_tj}(x_t), float64."""
     T, H, I, k = d.tokens, d.hidden, d.inter, d.topk
     tensor = getattr(d, "scaling", "block") == "tensor"
+    S = getattr(d, "num_shared", 0)
+    NE = d.num_local + S  # weight sets: routed local experts, then shared experts
     xs = np.zeros((T, H))
     xv = decode_e4m3_torch(inputs["x"])
     for t in range(T):
@@ -152,11 +154,11 @@ def layer_bruteforce(d, inputs):
             xs[t, c] = xv[t, c] * s
     if tensor:
         dec = decode_e4m3_torch if d.weight_format == "fp8" else decode_e5m2_torch
-        w1 = [dec(inputs["w1"][e]) * float(inputs["w1_sf"][e]) for e in range(d.num_local)]
-        w2 = [dec(inputs["w2"][e]) * float(inputs["w2_sf"][e]) for e in range(d.num_local)]
+        w1 = [dec(inputs["w1"][e]) * float(inputs["w1_sf"][e]) for e in range(NE)]
+        w2 = [dec(inputs["w2"][e]) * float(inputs["w2_sf"][e]) for e in range(NE)]
     else:
-        w1 = [weight_dense(inputs["w1"][e], inputs["w1_sf"][e], d.weight_format, 2 * I, H) for e in range(d.num_local)]
-        w2 = [weight_dense(inputs["w2"][e], inputs["w2_sf"][e], d.weight_format, H, I) for e in range(d.num_local)]
+        w1 = [weight_dense(inputs["w1"][e], inputs["w1_sf"][e], d.weight_format, 2 * I, H) for e in range(NE)]
+        w2 = [weight_dense(inputs["w2"][e], inputs["w2_sf"][e], d.weight_format, H, I) for e in range(NE)]
     y = np.zeros((T, H))
     for t in range(T):
         ids, ls = topk_bruteforce(inputs["logits"][t], k)
@@ -164,11 +166,10 @@ def layer_bruteforce(d, inputs):
         tot = 0.0
         for v in ex:
             tot += v
-        for j, e in enumerate(ids):
-            le = e - d.local_begin
-            if not (0 <= le < d.num_local):
-                continue
-            wt = float(np.float32(ex[j] / tot))
+        pairs = [(e - d.local_begin, float(np.float32(ex[j] / tot))) for j, e in enumerate(ids)]
+        pairs = [(le, wt) for le, wt in pairs if 0 <= le < d.num_local]  # local routed slots
+        pairs += [(d.num_local + s, 1.0) for s in range(S)]  # shared experts after them, weight 1
+        for le, wt in pairs:
             g = np.array([sum(xs[t, c] * w1[le][n, c] for c in range(H)) for n in range(I)])
             u = np.array([sum(xs[t, c] * w1[le][I + n, c] for c in range(H)) for n in range(I)])
             h = np.array([act_scalar(g[n], u[n], d.activation, d.act_clamp, d.act_alpha, d.act_up_bias)

@@ -55,19 +55,21 @@ def run_split(w, dev, variant=-1):
     d = B.desc_from_workload(w, variant)
     ws = B.alloc_workspace(d)
     T, k, EL, I = w.tokens, w.topk, w.num_local, w.inter
+    S = getattr(w, "num_shared", 0)
     ids, tw = i32(T, k), torch.empty((T, k), dtype=torch.float32, device="cuda")
     counts, offsets, r2s, s2r = i32(EL), i32(EL + 1), i32(T * k), i32(T * k)
     B.moe_route_permute(d, dev["logits"], ids, tw, counts, offsets, r2s, s2r, ws)
-    h = torch.empty((T * k, I), dtype=torch.uint8, device="cuda")
+    h = torch.empty((T * (k + S), I), dtype=torch.uint8, device="cuda")  # routed rows, then shared
     tensor = getattr(w, "scaling", "block") == "tensor"
-    h_sf = None if tensor else torch.empty((T * k, I // 128), dtype=torch.uint8, device="cuda")
+    h_sf = None if tensor else torch.empty((T * (k + S), I // 128), dtype=torch.uint8, device="cuda")
     B.moe_grouped_fc1_swiglu(d, dev["x"], dev["x_sf"], dev["w1"], dev["w1_sf"], offsets, r2s, h, h_sf, ws)
     y = torch.empty((T, w.hidden), dtype=torch.int16, device="cuda")
     B.moe_grouped_fc2_combine(d, h, h_sf, dev["w2"], dev["w2_sf"], offsets, r2s, s2r, tw, y, ws)
     torch.cuda.synchronize()
     R = int(offsets[-1].item())
-    hs = np.zeros((R, I // 128), np.uint8) if tensor else h_sf[:R].cpu().numpy()
-    return {"y_bf16": y.cpu().numpy().view(np.uint16), "h": h[:R].cpu().numpy(), "h_sf": hs,
+    NR = R + S * T
+    hs = np.zeros((NR, I // 128), np.uint8) if tensor else h_sf[:NR].cpu().numpy()
+    return {"y_bf16": y.cpu().numpy().view(np.uint16), "h": h[:NR].cpu().numpy(), "h_sf": hs,
             "R": R, "offsets": offsets.cpu().numpy(), "row_to_slot": r2s.cpu().numpy(),
             "slot_to_row": s2r.cpu().numpy(), "topk_ids": ids.cpu().numpy(), "topk_w": tw.cpu().numpy(),
             "counts": counts.cpu().numpy()}

@@ -64,7 +64,8 @@ def test_workspace_size_covers_capacity(L, i):
 @pytest.mark.parametrize("field,value", [("hidden", 100), ("inter", 0), ("num_experts", 0), ("num_experts", 2000),
                                          ("topk", 0), ("topk", 17), ("num_local", 0), ("local_begin", -1),
                                          ("num_tokens", -5), ("weight_format", 7), ("activation", 3),
-                                         ("variant", 5), ("scale_mode", 2)])
+                                         ("variant", 5), ("scale_mode", 2), ("num_shared", 5),
+                                         ("num_shared", -1)])
 def test_invalid_descriptor_rejected(L, field, value):
     d = B.desc_from_workload(synth.workload("tiny"))
     setattr(d, field, value)

@@ -31,7 +31,7 @@ def _sample_tokens(ref, w, n=12, seed=0):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["decode", "decode/fp8e5m2", "prefill_zipf", "mxfp4_large"])
+@pytest.mark.parametrize("name", ["decode", "decode/fp8e5m2", "decode/shared1", "prefill_zipf", "mxfp4_large"])
 def test_fullsize_sampled_parity(name):
     """The fused layer at full size.  Workloads of at most 256 tokens are checked on every
     token, larger ones on a seeded sample.
@@ -43,10 +43,12 @@ def test_fullsize_sampled_parity(name):
     of a token whose only local row it is moves that token's output by up to ~1e-2 relative.
     The requantised intermediate of the evaluated rows is checked separately (three-call path,
     whose output equals the fused one bit for bit)."""
-    base, _, fmt = name.partition("/")
+    base, _, var = name.partition("/")
     w = synth.workload(base)
-    if fmt:
-        w = synth.shrink(w, weight_format=fmt, name=name)
+    if var.startswith("shared"):
+        w = synth.shrink(w, num_shared=int(var[6:]), name=name)
+    elif var:
+        w = synth.shrink(w, weight_format=var, name=name)
     G.say(f"[fullsize] {name}: generating inputs")
     inp = synth.generate(w)
     ids, tw = O.route(inp["logits"], w.topk)
@@ -68,7 +70,8 @@ def test_fullsize_sampled_parity(name):
           f"{np.median(per_tok):.3e} max {per_tok.max():.3e}")
     assert err <= TOL
     nol = (ref_route["slot_to_row"].reshape(w.tokens, w.topk) >= 0).sum(1) == 0
-    assert np.all(got["y_bf16"][nol] == 0)
+    if w.num_shared == 0:
+        assert np.all(got["y_bf16"][nol] == 0)
     split = G.run_split(w, dev)
     assert np.array_equal(split["y_bf16"], got["y_bf16"])
     be, se = G.h_agreement(split["h"], split["h_sf"], ref["h"], ref["h_sf"], ref["h_valid"])

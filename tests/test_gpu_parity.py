@@ -46,6 +46,11 @@ def _small_cases():
         ("tensor_e5m2_sat", synth.tensor_scaled(synth.shrink(oai, tokens=200, hidden=512, inter=256, num_experts=16,
                                                              local_begin=4, num_local=8, topk=4,
                                                              weight_format="fp8e5m2", seed=17), h_scale=0.0015)),
+        # shared experts after the routed ones (weight 1 for every token)
+        ("shared_oai", synth.shrink(oai, tokens=300, hidden=768, inter=384, num_experts=16, local_begin=4,
+                                    num_local=8, topk=4, num_shared=1, seed=18)),
+        ("shared2_partial", synth.shrink(tiny, tokens=40, hidden=512, inter=256, num_experts=64, local_begin=10,
+                                         num_local=8, topk=4, num_shared=2, seed=19)),
         ("top1", synth.shrink(tiny, tokens=130, topk=1, seed=11)),
         ("k16_e1024", synth.shrink(tiny, tokens=40, num_experts=1024, local_begin=1000, num_local=24, topk=16,
                                    seed=12)),
@@ -77,14 +82,17 @@ def test_layer_parity_small(name, w):
     fused = G.run_layer(w, dev)
     assert np.array_equal(fused["y_bf16"], got["y_bf16"])
     G.check_routing(fused, ref)
-    # tokens without a local slot are exactly +0
+    # without shared experts, tokens without a local slot are exactly +0
     nol = ~(ref["slot_to_row"].reshape(w.tokens, w.topk) >= 0).any(1)
-    assert np.all(fused["y_bf16"][nol] == 0)
+    if w.num_shared == 0:
+        assert np.all(fused["y_bf16"][nol] == 0)
+    else:
+        assert nol.any() or name != "shared2_partial"
 
 
 @pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("name", ["ragged_oai", "ragged_h384_share", "zipf_small", "mxfp4_small", "e5m2_small",
-                                  "tensor_oai", "k16_e1024"])
+                                  "tensor_oai", "shared_oai", "k16_e1024"])
 def test_layer_parity_forced_variant(name, variant):
     w = dict(_small_cases())[name]
     G.say(f"[variant] {name} variant={variant}")

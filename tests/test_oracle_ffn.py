@@ -178,3 +178,40 @@ def test_tokens_without_local_slot_are_zero():
     loc = (out["slot_to_row"].reshape(d.tokens, d.topk) >= 0).any(1)
     assert (~loc).sum() > 0
     assert np.all(out["y64"][~loc] == 0)
+
+
+@pytest.mark.parametrize("d", [
+    _tiny(num_shared=1, seed=31),
+    # shared experts on top of a partial local share (some tokens have no routed local slot)
+    _tiny(num_experts=8, local_begin=5, num_local=2, topk=2, num_shared=2, activation="swigluoai", act_clamp=7.0,
+          act_alpha=1.702, act_up_bias=1.0, seed=32),
+    synth.tensor_scaled(_tiny(num_shared=1, weight_format="fp8e5m2", seed=33)),
+])
+def test_shared_experts_match_token_by_token_bruteforce(d):
+    inp = synth.generate(d)
+    assert inp["w1"].shape[0] == d.num_local + d.num_shared
+    out = O.layer(d, inp)
+    ref = brute.layer_bruteforce(d, inp)
+    err = np.abs(out["y64"] - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err < 1e-12
+    assert np.array_equal(out["y_bf16"], O.bf16_rne_bits(ref))
+    assert out["h"].shape[0] == out["R"] + d.num_shared * d.tokens
+
+
+def test_shared_expert_equals_routing_every_token_to_it():
+    """A shared expert is the same computation as a routed expert that every token picks with
+    weight exactly 1 (top-1 over a single local expert whose logit always wins)."""
+    d = _tiny(tokens=16, num_local=4, num_shared=1, seed=34)
+    inp = synth.generate(d)
+    out = O.layer(d, inp)
+    # the shared expert alone: zero the routed part by routing every token to a non-local expert
+    d1 = synth.shrink(d, num_experts=5, local_begin=4, num_local=1, topk=1, num_shared=0)
+    inp1 = dict(inp)
+    inp1["logits"] = np.zeros((d.tokens, 5), np.float32)
+    inp1["logits"][:, 4] = 10.0  # expert 4 (the only local one) wins for every token
+    for key in ("w1", "w1_sf", "w2", "w2_sf"):
+        inp1[key] = inp[key][4:5]  # the shared expert's weights as local expert 4
+    only_shared = O.layer(d1, inp1)
+    assert np.all(only_shared["topk_w"] == 1.0)
+    routed = O.layer(synth.shrink(d, num_shared=0), {k: (v[:4] if k.startswith("w") else v) for k, v in inp.items()})
+    assert np.allclose(out["y64"], routed["y64"] + only_shared["y64"], rtol=0, atol=1e-12 * np.abs(out["y64"]).max())
