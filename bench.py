@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer TFLOPS & tokens/s at 128-32768 tok/GPU; % of FP8 MFMA / HBM peak"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (published, no sparsity)
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
@@ -37,13 +38,16 @@ def source_hash() -> str:
 def algorithmic(w, R, active, counts):
     """Useful FLOPs and bytes of the layer and of FC1 / FC2 for this routing."""
     H, I, T, E = w.hidden, w.inter, w.tokens, w.num_experts
-    if w.weight_format != "mxfp4":
+    if w.weight_format == "bf16":  # two bytes per element, no scales
+        wb = lambda n, k: n * k * 2.0
+    elif w.weight_format != "mxfp4":
         wb = lambda n, k: n * k * (1 + 1 / 16384)
     else:
         wb = lambda n, k: n * k * (0.5 + 1 / 32)
     fl1, fl2 = 4.0 * R * H * I, 2.0 * R * H * I
-    x_bytes = T * H * (1 + 1 / 128)
-    h_bytes = R * I * (1 + 1 / 128)
+    eb = (2.0, 0.0) if w.weight_format == "bf16" else (1.0, 1 / 128)  # element bytes, scale bytes per element
+    x_bytes = T * H * (eb[0] + eb[1])
+    h_bytes = R * I * (eb[0] + eb[1])
     b1 = active * wb(2 * I, H) + x_bytes + h_bytes
     b2 = active * wb(H, I) + h_bytes + R * H * 4
     layer_bytes = active * (wb(2 * I, H) + wb(H, I)) + x_bytes + 2 * T * H + 4 * T * E
@@ -85,8 +89,8 @@ def main():
     ap.add_argument("--config", default="oai", help="workload name or index (tiny, oai, decode, prefill_zipf, "
                                                      "mxfp4_large)")
     ap.add_argument("--variant", type=int, default=-1)
-    ap.add_argument("--weights", choices=["fp8", "fp8e5m2", "mxfp4"], default=None,
-                    help="replace the workload's weight format (FP8 E4M3, FP8 E5M2 or MXFP4)")
+    ap.add_argument("--weights", choices=["fp8", "fp8e5m2", "mxfp4", "bf16"], default=None,
+                    help="replace the workload's weight format (FP8 E4M3, FP8 E5M2, MXFP4, or the BF16 layer)")
     ap.add_argument("--shared", type=int, default=0, help="shared experts (every token, weight 1)")
     ap.add_argument("--scaling", choices=["block", "tensor"], default="block",
                     help="blockwise UE8M0 scales, or one float32 scale per tensor (FP8 weights)")
@@ -130,7 +134,7 @@ def main():
     t0 = time.time()
     inp = synth.generate(w)
     print(f"[bench] generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    dev = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    dev = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda() for k, v in inp.items()}
     d = B.desc_from_workload(w, args.variant)
     ws = B.alloc_workspace(d)
     T, k, EL = w.tokens, w.topk, w.num_local
@@ -175,7 +179,8 @@ def main():
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
     B.moe_route_permute(d, dev["logits"], ids, tw, counts, offsets, r2s, s2r, ws, stream=stream)
-    h = torch.empty((T * (k + S), w.inter), dtype=torch.uint8, device="cuda")
+    h_dtype = torch.int16 if w.weight_format == "bf16" else torch.uint8  # BF16 layer: two bytes per value
+    h = torch.empty((T * (k + S), w.inter), dtype=h_dtype, device="cuda")
     h_sf = torch.empty((T * (k + S), w.inter // 128), dtype=torch.uint8, device="cuda")
     for i in range(3):
         w1, w1s, _, _ = wsets[i % len(wsets)]
@@ -191,7 +196,7 @@ def main():
 
     compute_bound = w.tokens >= 2048
     if compute_bound:
-        peak = PEAK_FP8_TFLOPS
+        peak = PEAK_BF16_TFLOPS if w.weight_format == "bf16" else PEAK_FP8_TFLOPS
         achieved = alg["fc1_flops"] / (fc1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s"}
     else:
@@ -233,13 +238,15 @@ def main():
     out = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4" if w.weight_format == "mxfp4" else "fp8",
+        "scaling": "weak", "vs_baseline": None, "dtype": {"mxfp4": "fp8xfp4", "bf16": "bf16"}.get(w.weight_format, "fp8"),
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden": w.hidden, "inter": w.inter,
                    "experts": w.num_experts, "local_experts": EL, "topk": k, "activation": w.activation,
                    "weight_format": w.weight_format, "scaling": w.scaling, "shared_experts": S, "rows": R, "active_experts": active,
                    "parallelism": "one GPU's expert share", "weight_copies": len(wsets)},
         "tflops": round(tflops, 2), "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+        "pct_mfma_peak_of_dtype": round(100 * tflops / (PEAK_BF16_TFLOPS if w.weight_format == "bf16"
+                                                        else PEAK_FP8_TFLOPS), 2),
         "hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
         "pct_hbm_peak": round(100 * alg["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "wall_ms_timed_region": round(wall_ms, 2),

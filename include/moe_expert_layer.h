@@ -56,6 +56,13 @@
  *                   h_scale (> 0, finite) is the static scale in the descriptor and
  *                   h_sf is neither read nor written (it may be NULL)
  *     Non-finite or non-positive tensor scales give unspecified results.
+ *   - BF16 layer (weight_format = MOE_W_BF16; the pages list BF16 Mega MoE builds beside
+ *     the FP8/FP4 ones, "Sync upstream through PR #441"): x is bfloat16 bits [T, H], w1
+ *     bfloat16 [E_loc, 2I, H], w2 bfloat16 [E_loc, H, I], h bfloat16 [rows, I] (each
+ *     pointer still passed as bytes: rows are 2H, 2I bytes); h is the activation rounded
+ *     once to bfloat16 (round to nearest even); x_sf, w1_sf, w2_sf and h_sf are not read
+ *     or written (they may be NULL).  Blockwise scaling mode only; x smaller than 4 GiB
+ *     means T*H < 2^31 here.
  *   - Shared experts (num_shared = S > 0; the pages list shared-expert builds of the
  *     kernel, "Sync upstream through PR #441", Validation): S more experts that every token
  *     passes through with weight 1.  Their weights follow the routed local experts in
@@ -111,7 +118,12 @@ typedef enum { MOE_SCALE_BLOCK = 0, MOE_SCALE_TENSOR = 1 } moe_scale;
 /* Weight formats: FP8 E4M3 or E5M2 with 128x128 UE8M0 block scales, or MXFP4 (E2M1, UE8M0
  * per 32 along K).  The FP8 weight formats are the ones the Hopper CuTeDSL MegaMoE kernel
  * takes (Pull Style Cutedsl Megakernel, Layout section); the activations stay E4M3. */
-typedef enum { MOE_W_FP8_E4M3_B128 = 0, MOE_W_MXFP4_E2M1_B32 = 1, MOE_W_FP8_E5M2_B128 = 2 } moe_wfmt;
+typedef enum {
+  MOE_W_FP8_E4M3_B128 = 0,
+  MOE_W_MXFP4_E2M1_B32 = 1,
+  MOE_W_FP8_E5M2_B128 = 2,
+  MOE_W_BF16 = 3  /* BF16 layer: x, weights and h in BF16, no scales (see above) */
+} moe_wfmt;
 
 typedef struct {
   int32_t num_tokens;     /* T >= 0 */

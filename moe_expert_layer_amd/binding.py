@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(PKG, "libmoe_expert_layer.so")
 MOE_OK, MOE_ERR_NULL, MOE_ERR_INVALID_DESC, MOE_ERR_MISALIGNED, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, \
     MOE_ERR_DEVICE = range(7)
 MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = 0, 1
-MOE_W_FP8_E4M3_B128, MOE_W_MXFP4_E2M1_B32, MOE_W_FP8_E5M2_B128 = 0, 1, 2
+MOE_W_FP8_E4M3_B128, MOE_W_MXFP4_E2M1_B32, MOE_W_FP8_E5M2_B128, MOE_W_BF16 = 0, 1, 2, 3
 ACTIVATIONS = {"swiglu": MOE_ACT_SWIGLU, "swigluoai": MOE_ACT_SWIGLU_OAI}
 MOE_SCALE_BLOCK, MOE_SCALE_TENSOR = 0, 1
 SCALINGS = {"block": MOE_SCALE_BLOCK, "tensor": MOE_SCALE_TENSOR}
-WEIGHT_FORMATS = {"fp8": MOE_W_FP8_E4M3_B128, "mxfp4": MOE_W_MXFP4_E2M1_B32, "fp8e5m2": MOE_W_FP8_E5M2_B128}
+WEIGHT_FORMATS = {"fp8": MOE_W_FP8_E4M3_B128, "mxfp4": MOE_W_MXFP4_E2M1_B32, "fp8e5m2": MOE_W_FP8_E5M2_B128, "bf16": MOE_W_BF16}
 
 
 class MoeLayerDesc(ctypes.Structure):

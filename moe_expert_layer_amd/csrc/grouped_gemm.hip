@@ -49,6 +49,14 @@
 namespace moe {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// half q (16 bytes) of a lane's 32-byte operand fragment as 8 BF16 values
+__device__ __forceinline__ bf16x8 bf16_half(const v8i& v, int q) {
+  const v4i h = q == 0 ? __builtin_shufflevector(v, v, 0, 1, 2, 3) : __builtin_shufflevector(v, v, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, h);
+}
 
 constexpr int kGroupN = 8;     // n-tiles per group in the tile order
 constexpr int kMaxKSteps = 64; // K <= 8192 (scales of a tile are staged in LDS, one per 128-wide step)
@@ -93,6 +101,8 @@ struct Cfg {
   static constexpr int WM = BM / WTM;                       // waves along M
   static constexpr int WN = NW / WM;                        // waves along N
   static constexpr int MI = WTM / 32;                       // 32-row tiles per wave
+  // BK is in bytes of an operand row per stage: 128 FP8 or 64 BF16 elements for BK = 128
+  static constexpr bool BF16 = WFMT == 3;                   // BF16 operands, unscaled MFMA
   static constexpr int A_ROWB = BK;                         // bytes per activation row per stage
   static constexpr int B_ROWB = WFMT == 1 ? BK / 2 : BK;    // bytes per weight row per stage
   // weight operand format code of the scaled MFMA: E4M3 0, E5M2 1, E2M1 4
@@ -109,7 +119,7 @@ struct Cfg {
   static constexpr int S_DMA = WFMT == 1 ? 1 : 0;           // 4-byte DMA instructions per wave per stage
   static constexpr int PER_STAGE = A_DMA + B_DMA + S_DMA;
   static constexpr int NT = BN / WN / 32;                   // 32-wide column tiles per wave
-  static constexpr int NH = BK / 64;                        // 64-wide MFMA K steps per stage
+  static constexpr int NH = BK / 64;  // 64-byte K steps per stage (one FP8 MFMA or two BF16 ones)
   static constexpr int A_CPR = A_ROWB / 16, B_CPR = B_ROWB / 16;  // 16-byte chunks per row
   static_assert(WM * WN == NW && NT >= 1 && (MODE == 2 || NT % 2 == 0), "waves must cover the tile");
   static_assert(A_INSTR >= 1 && B_DMA >= 1 && B_DMA * NW * 1024 == B_BYTES, "");
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   uint8_t* ring = lds;
   uint8_t* s_asf = lds + NSTAGE * C::STAGE;
-  const int nk128_ = g.K / 128;
+  const int nk128_ = C::BF16 ? 0 : g.K / 128;
   uint8_t* s_bsf = s_asf + BM * nk128_;
   int* s_tok = reinterpret_cast<int*>(ring + NSTAGE * C::STAGE - BM * 4);  // prologue only
   float(*s_amax)[BM] = reinterpret_cast<float(*)[BM]>(ring + BM * 128);      // epilogue only
@@ -246,8 +256,9 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = BM == 256 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int wm = wave % C::WM, wn = wave / C::WM;
-  const int nk = g.K / BK;       // stages
-  const int nk128 = g.K / 128;   // scale steps
+  const int Kb = C::BF16 ? 2 * g.K : g.K;  // bytes per operand row (FP8: K, BF16: 2K)
+  const int nk = Kb / BK;                  // stages
+  const int nk128 = g.K / 128;             // scale steps (scaled formats)
   const int n0 = MODE == 1 ? n_tile * 128 : n_tile * BN;
 
   // ---- tile rows: the token (FC1; row i of a shared expert is token i) or h row (FC2) of
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   // FP8 weight scales of the tile's two 128-row blocks (FC1: gate n0/128 and up (I+n0)/128;
   // FC2: n0/128 and n0/128 + 1, clamped), loaded now and written to LDS after the DMA issue
   const uint8_t* bsf_e = g.B_sf + (long long)e * g.bsf_estride;
-  const bool bsf_mine = WFMT != 1 && tid < 2 * nk128;
+  const bool bsf_mine = WFMT != 1 && !C::BF16 && tid < 2 * nk128;
   int bsf_v = 0;
   if (bsf_mine) {
     const int blk = tid / nk128, ks = tid - blk * nk128;
@@ -270,7 +281,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   // activation scales of the tile rows in LDS as [row][k step]: moved by 4-byte DMA when a
   // row is whole dwords (nk128 % 4 == 0), else by byte loads
   const uint8_t* asf_gbase = MODE == 1 ? g.A_sf : g.A_sf + (long long)row_begin * nk128;
-  const bool asf_dma = !g.tensor && (nk128 & 3) == 0 && ((BM * nk128) & 255) == 0;
+  const bool asf_dma = !C::BF16 && !g.tensor && (nk128 & 3) == 0 && ((BM * nk128) & 255) == 0;
   constexpr int kAsfDma = (BM * kMaxKSteps / 256 + NW - 1) / NW;  // 64-lane DMAs per wave, at most
   const int asf_n = BM * nk128 / 256;                               // 64-lane DMAs of the tile
   uint32_t asf_off[kAsfDma];
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
       const int q = (wave + NW * j) * 64 + lane, row = min(q / dpr, BM - 1);
       asf_off[j] = (uint32_t)(s_tok[row] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)nk128 + (uint32_t)(q - row * dpr) * 4u;
     }
-  } else {
+  } else if (!C::BF16) {
     for (int i = tid; i < nk128 * BM; i += C::NTHR) {
       const int r = i / nk128;
       s_asf[i] = g.tensor ? 127 : asf_gbase[(long long)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * nk128 + (i - r * nk128)];
@@ -291,13 +302,13 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   // ---- DMA sources of this lane (offsets from uniform bases), swizzled chunk folded in ----
   // FC1 gathers token rows of x (offsets below 2^32: x is smaller than 4 GiB); FC2 reads the
   // tile's rows of h from the tile's first row
-  const uint8_t* a_gbase = MODE == 1 ? g.A : g.A + (long long)row_begin * g.K;
+  const uint8_t* a_gbase = MODE == 1 ? g.A : g.A + (long long)row_begin * Kb;
   uint32_t a_off[C::A_DMA];
 #pragma unroll
   for (int j = 0; j < C::A_DMA; ++j) {
     const int r = ((wave * C::A_DMA + j) % C::A_INSTR) * (64 / C::A_CPR) + lane / C::A_CPR;
     const int c = (lane % C::A_CPR) ^ swz<C::A_CPR>(r);
-    a_off[j] = (uint32_t)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)g.K + (uint32_t)(c * 16);
+    a_off[j] = (uint32_t)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)Kb + (uint32_t)(c * 16);
   }
   const uint8_t* b_e = g.B + (long long)e * g.b_estride;
   auto b_row = [&](int n) -> int {
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
     const int rr = n0 + n;
     return rr < g.N ? rr : g.N - 1;
   };
-  const uint32_t b_ld = WFMT == 1 ? g.K / 2 : g.K;
+  const uint32_t b_ld = WFMT == 1 ? g.K / 2 : Kb;
   uint32_t b_off[C::B_DMA];
 #pragma unroll
   for (int j = 0; j < C::B_DMA; ++j) {
@@ -384,10 +395,12 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
     const uint8_t* st = ring + (ks % NSTAGE) * C::STAGE;
     const uint8_t* sb_ = st + C::A_BYTES;
     const int k128 = (ks * BK) / 128;
+    if (!C::BF16) {
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) f.sa[mi] = s_asf[(ra + mi * 32) * nk128 + k128];
+      for (int mi = 0; mi < C::MI; ++mi) f.sa[mi] = s_asf[(ra + mi * 32) * nk128 + k128];
+    }
     int sbu0 = 0, sbu1 = 0;
-    if (WFMT != 1) {  // one weight scale per 128x128 block
+    if (WFMT != 1 && !C::BF16) {  // one weight scale per 128x128 block
       if (MODE == 1) { sbu0 = s_bsf[k128]; sbu1 = s_bsf[nk128 + k128]; }
       else { sbu0 = s_bsf[(wn * (BN / C::WN)) / 128 * nk128 + k128]; sbu1 = sbu0; }
     }
@@ -434,14 +447,26 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
 #pragma unroll
       for (int ct = 0; ct < C::NT; ++ct)
 #pragma unroll
-        for (int mi = 0; mi < NL; ++mi)
-          acc[mi][ct] = MODE == 1
-                            ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[h][ct], f.a[h][mi], acc[mi][ct],
-                                                                              C::WCODE, 0, 0, f.sb[h][ct],
-                                                                              0, f.sa[mi])
-                            : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[h][mi], f.b[h][ct], acc[mi][ct], 0,
-                                                                              C::WCODE, 0, f.sa[mi], 0,
-                                                                              f.sb[h][ct]);
+        for (int mi = 0; mi < NL; ++mi) {
+          if constexpr (C::BF16) {
+            // the 32 bytes of a lane are two 16-wide K steps of 8 BF16 values each (chunks kb
+            // and 2 + kb of the 64-byte step), one unscaled 32x32x16 MFMA each
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const bf16x8 a = bf16_half(f.a[h][mi], q), b = bf16_half(f.b[h][ct], q);
+              acc[mi][ct] = MODE == 1 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[mi][ct], 0, 0, 0)
+                                      : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[mi][ct], 0, 0, 0);
+            }
+          } else {
+            acc[mi][ct] = MODE == 1
+                              ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[h][ct], f.a[h][mi], acc[mi][ct],
+                                                                                C::WCODE, 0, 0, f.sb[h][ct],
+                                                                                0, f.sa[mi])
+                              : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[h][mi], f.b[h][ct], acc[mi][ct],
+                                                                                0, C::WCODE, 0, f.sa[mi], 0,
+                                                                                f.sb[h][ct]);
+          }
+        }
   };
   const int live_tiles = min(C::MI, max(0, (rows - wm * WTM + 31) / 32));
   auto mma = [&](const auto& f) {
@@ -583,6 +608,37 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
           acc[mi][c][i] = gt * sigmoidf_(gt) * acc[mi][c + NC][i];
         }
   }
+  if constexpr (C::BF16) {
+    // ---- BF16 layer: h is the activation rounded once to BF16 (no scale).  Four
+    //      consecutive columns per lane go to a [BM rows][256 B] tile with 16-byte chunks
+    //      XOR-swizzled by row, then whole 16-byte chunks go out row by row ----
+    __syncthreads();  // every wave is past its last ring read
+    uint8_t* stage_h = ring;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int r = trow + mi * 32;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[mi][c][4 * q]) |
+                              ((uint32_t)f32_to_bf16_rne(acc[mi][c][4 * q + 1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[mi][c][4 * q + 2]) |
+                              ((uint32_t)f32_to_bf16_rne(acc[mi][c][4 * q + 3]) << 16);
+          const int col = wn * (128 / C::WN) + c * 32 + 8 * q + 4 * kb;  // multiple of 4
+          *reinterpret_cast<uint2*>(stage_h + r * 256 + ((((col >> 3) ^ (r & 15)) << 4) | ((col & 7) * 2))) =
+              make_uint2(lo, hi);
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < BM * 16; q += C::NTHR) {
+      const int r = q >> 4, c = q & 15;
+      if (r < rows)
+        *reinterpret_cast<uint4*>(g.h + (long long)(row_begin + r) * (2 * g.I) + 2 * n0 + c * 16) =
+            *reinterpret_cast<const uint4*>(stage_h + r * 256 + ((c ^ (r & 15)) << 4));
+    }
+    return;
+  }
   // amax of each row: over the lane's values (an unsigned max of the non-negative float
   // bits), then with lane l ^ 32 (the other half of the columns), then across the WN waves
   // through LDS.  Both lanes of a pair write the same value to the same place.
@@ -670,7 +726,8 @@ bool gemm_supports(int H, int I) { return H / 128 <= kMaxKSteps && I / 128 <= kM
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
 static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
-  static_assert(NSTAGE * C::STAGE >= BM * 128 + C::WN * BM * 4 + BM && NSTAGE * C::STAGE >= BM * 4 + BM * 128,
+  static_assert(NSTAGE * C::STAGE >= BM * 128 + C::WN * BM * 4 + BM && NSTAGE * C::STAGE >= BM * 4 + BM * 128 &&
+                    (!C::BF16 || NSTAGE * C::STAGE >= BM * 256),
                 "the ring must hold the epilogue staging and the tile's token list");
   auto kern = grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   const size_t lds = (size_t)NSTAGE * C::STAGE + (size_t)BM * (a.K / 128) + 2 * (a.K / 128);
@@ -704,11 +761,13 @@ static hipError_t launch_variant_w(const GemmArgs& a, int variant, size_t grid, 
   else return launch_one<MODE, WFMT, 128, 256, 64, 3, 4, 64, 0>(a, grid, s);
 }
 
-// weight formats: 0 FP8 E4M3 with 128x128 scales, 1 MXFP4, 2 FP8 E5M2 with 128x128 scales
+// weight formats: 0 FP8 E4M3 with 128x128 scales, 1 MXFP4, 2 FP8 E5M2 with 128x128 scales,
+// 3 BF16 (activations, weights and the intermediate all BF16, no scales)
 template <int MODE>
 static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_t grid, hipStream_t s) {
   if (wfmt == 1) return launch_variant_w<MODE, 1>(a, variant, grid, s);
   if (wfmt == 2) return launch_variant_w<MODE, 2>(a, variant, grid, s);
+  if (wfmt == 3) return launch_variant_w<MODE, 3>(a, variant, grid, s);
   return launch_variant_w<MODE, 0>(a, variant, grid, s);
 }
 
@@ -730,7 +789,8 @@ hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint
   // the permute's tile plan covers the routed experts only
   a.offsets = offsets; a.plan = plan_ready && sh.S == 0 ? plan : nullptr; a.h = h; a.h_sf = h_sf;
   a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.S = sh.S; a.T = sh.T; a.n_tiles = sh.I / 128;
-  a.b_estride = sh.wfmt != 1 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
+  a.b_estride = sh.wfmt == 3 ? (long long)2 * sh.I * sh.H * 2
+                : sh.wfmt != 1 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
   a.act = sh.act; a.clamp = sh.clamp; a.alpha = sh.alpha; a.bias = sh.bias;
   set_tensor_scales(a, sh, reinterpret_cast<const float*>(x_sf), reinterpret_cast<const float*>(w1_sf));
@@ -748,7 +808,7 @@ hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint
   a.plan = plan_ready && sh.S == 0 ? plan : nullptr;
   a.y2 = y2;
   a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.S = sh.S; a.T = sh.T;
-  a.b_estride = sh.wfmt != 1 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
+  a.b_estride = sh.wfmt == 3 ? (long long)sh.H * sh.I * 2 : sh.wfmt != 1 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
   set_tensor_scales(a, sh, nullptr, reinterpret_cast<const float*>(w2_sf));
   const int bn = variant == 0 ? 128 : 256;

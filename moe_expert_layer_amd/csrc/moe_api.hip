@@ -71,7 +71,7 @@ Layout make_layout(const moe_layer_desc& d) {
   L.chunk_base = take(nchunks * NB * 4);
   L.plan1 = take(NB * 4);
   const size_t hrows = cap + (size_t)d.num_shared * d.num_tokens;  // routed rows, then shared experts' rows
-  L.h = take(hrows * (size_t)d.inter);
+  L.h = take(hrows * (size_t)d.inter * (d.weight_format == MOE_W_BF16 ? 2 : 1));
   L.h_sf = take(hrows * (size_t)(d.inter / 128));
   L.y2 = take(hrows * (size_t)d.hidden * 4);
   L.total = at;
@@ -95,7 +95,7 @@ moe_status check_desc(const moe_layer_desc* d) {
   if ((long long)d->num_tokens * d->topk * d->hidden >= (1LL << 46))
     return fail(MOE_ERR_INVALID_DESC, "num_tokens * topk * hidden too large");
   if (d->weight_format != MOE_W_FP8_E4M3_B128 && d->weight_format != MOE_W_MXFP4_E2M1_B32 &&
-      d->weight_format != MOE_W_FP8_E5M2_B128)
+      d->weight_format != MOE_W_FP8_E5M2_B128 && d->weight_format != MOE_W_BF16)
     return fail(MOE_ERR_INVALID_DESC, "weight_format %d unknown", d->weight_format);
   if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_SWIGLU_OAI)
     return fail(MOE_ERR_INVALID_DESC, "activation %d unknown", d->activation);
@@ -113,16 +113,16 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->scale_mode != MOE_SCALE_BLOCK && d->scale_mode != MOE_SCALE_TENSOR)
     return fail(MOE_ERR_INVALID_DESC, "scale_mode %d unknown", d->scale_mode);
   if (d->scale_mode == MOE_SCALE_TENSOR) {
-    if (d->weight_format == MOE_W_MXFP4_E2M1_B32)
+    if (d->weight_format == MOE_W_MXFP4_E2M1_B32 || d->weight_format == MOE_W_BF16)
       return fail(MOE_ERR_INVALID_DESC, "per-tensor scaling needs FP8 weights");
     if (!std::isfinite(d->h_scale) || !(d->h_scale > 0.f))
       return fail(MOE_ERR_INVALID_DESC, "h_scale must be finite and > 0");
   }
   if (!moe::gemm_supports(d->hidden, d->inter))
     return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d above the supported 8192", d->hidden, d->inter);
-  if ((long long)d->num_tokens * d->hidden >= (1LL << 32))
-    return fail(MOE_ERR_UNSUPPORTED, "x of num_tokens * hidden = %lld bytes is 4 GiB or more",
-                (long long)d->num_tokens * d->hidden);
+  const long long x_bytes = (long long)d->num_tokens * d->hidden * (d->weight_format == MOE_W_BF16 ? 2 : 1);
+  if (x_bytes >= (1LL << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "x of %lld bytes is 4 GiB or more", x_bytes);
   return MOE_OK;
 }
 
@@ -268,8 +268,8 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* d, const uint8_t* x, con
                                   uint8_t* h_sf, void* ws, size_t ws_bytes, void* stream) {
   if (moe_status st = check_desc(d)) return st;
   if (d->num_tokens == 0) return ok();
-  const bool tensor = d->scale_mode == MOE_SCALE_TENSOR;
-  if (!x || !x_sf || !w1 || !w1_sf || !offsets || !r2s || !h || (!h_sf && !tensor))
+  const bool tensor = d->scale_mode == MOE_SCALE_TENSOR, bf16 = d->weight_format == MOE_W_BF16;
+  if (!x || (!x_sf && !bf16) || !w1 || (!w1_sf && !bf16) || !offsets || !r2s || !h || (!h_sf && !tensor && !bf16))
     return fail(MOE_ERR_NULL, "a required pointer is NULL");
   if (misaligned(x, 16) || misaligned(w1, 16) || misaligned(h, 16) || misaligned(x_sf, 16) || misaligned(w1_sf, 16))
     return fail(MOE_ERR_MISALIGNED, "x / x_sf / w1 / w1_sf / h not 16-byte aligned");
@@ -288,8 +288,8 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* d, const uint8_t* h, co
                                    void* stream) {
   if (moe_status st = check_desc(d)) return st;
   if (d->num_tokens == 0) return ok();
-  const bool tensor = d->scale_mode == MOE_SCALE_TENSOR;
-  if (!h || (!h_sf && !tensor) || !w2 || !w2_sf || !offsets || !r2s || !s2r || !w || !y)
+  const bool tensor = d->scale_mode == MOE_SCALE_TENSOR, bf16 = d->weight_format == MOE_W_BF16;
+  if (!h || (!h_sf && !tensor && !bf16) || !w2 || (!w2_sf && !bf16) || !offsets || !r2s || !s2r || !w || !y)
     return fail(MOE_ERR_NULL, "a required pointer is NULL");
   if (misaligned(h, 16) || misaligned(w2, 16) || misaligned(y, 16) || misaligned(h_sf, 16) || misaligned(w2_sf, 16))
     return fail(MOE_ERR_MISALIGNED, "h / h_sf / w2 / w2_sf / y not 16-byte aligned");
@@ -311,7 +311,9 @@ moe_status moe_layer(const moe_layer_desc* d, const float* logits, const uint8_t
                      int32_t* opt_s2r, void* ws, size_t ws_bytes, void* stream) {
   if (moe_status st = check_desc(d)) return st;
   if (d->num_tokens == 0) return ok();
-  if (!logits || !x || !x_sf || !w1 || !w1_sf || !w2 || !w2_sf || !y) return fail(MOE_ERR_NULL, "a required pointer is NULL");
+  const bool bf16 = d->weight_format == MOE_W_BF16;  // no scale tensors
+  if (!logits || !x || (!x_sf && !bf16) || !w1 || (!w1_sf && !bf16) || !w2 || (!w2_sf && !bf16) || !y)
+    return fail(MOE_ERR_NULL, "a required pointer is NULL");
   if (misaligned(logits, 16) || misaligned(x, 16) || misaligned(x_sf, 16) || misaligned(w1, 16) ||
       misaligned(w1_sf, 16) || misaligned(w2, 16) || misaligned(w2_sf, 16) || misaligned(y, 16))
     return fail(MOE_ERR_MISALIGNED, "an input/output pointer is not 16-byte aligned");

@@ -46,7 +46,7 @@ class Workload:
     act_clamp: float
     act_alpha: float
     act_up_bias: float
-    weight_format: str  # "fp8" (E4M3) | "fp8e5m2" | "mxfp4"
+    weight_format: str  # "fp8" (E4M3) | "fp8e5m2" | "mxfp4" | "bf16" (x, weights, h all BF16)
     routing: str  # "normal" | "zipf"
     zipf_s: float
     seed: int
@@ -198,9 +198,13 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: 
     if w.scaling not in ("block", "tensor"):
         raise ValueError(f"unknown scaling {w.scaling}")
     tensor = w.scaling == "tensor"
-    if tensor and w.weight_format == "mxfp4":
+    if tensor and w.weight_format in ("mxfp4", "bf16"):
         raise ValueError("per-tensor scaling needs FP8 weights")
-    if tensor:
+    bf16 = w.weight_format == "bf16"
+    if bf16:  # BF16 layer: bit patterns, no scale tensors
+        x = (xf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        x_sf = np.zeros(0, np.uint8)
+    elif tensor:
         x, xs = _quant_fp8_tensor(xf)
         x_sf = np.array([xs], np.float32)
     else:
@@ -209,7 +213,7 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: 
     if with_bf16:
         out["x_bf16"] = (xf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     del xf
-    if w.weight_format not in ("fp8", "fp8e5m2", "mxfp4"):
+    if w.weight_format not in ("fp8", "fp8e5m2", "mxfp4", "bf16"):
         raise ValueError(f"unknown weight format {w.weight_format}")
     fp8 = w.weight_format != "mxfp4"
     f8 = "e5m2" if w.weight_format == "fp8e5m2" else "e4m3"
@@ -222,10 +226,18 @@ def generate(w: Workload, seed: int | None = None, threads: int = 8, with_bf16: 
     if tensor:
         w2_sf = np.empty(EL, np.float32)
 
+    if bf16:
+        w1 = np.empty((EL, 2 * I, H), np.uint16)
+        w2 = np.empty((EL, H, I), np.uint16)
+        w1_sf = w2_sf = np.zeros(0, np.uint8)
+
     def one(e):
         for which, shape, dst, dsf in ((0, (2 * I, H), w1, w1_sf), (1, (H, I), w2, w2_sf)):
             a = rng(2 + 2 * e + which).standard_normal(shape, dtype=np.float32)
             a *= np.float32(0.02)
+            if bf16:
+                dst[e] = (_bf16_round(a).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+                continue
             if tensor:
                 q, s = _quant_fp8_tensor(a, f8)
             else:

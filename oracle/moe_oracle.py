@@ -21,6 +21,8 @@ one GPU's share of the experts, written from the pages' description of the fused
   combine    top-k weighted sum of each token's local rows, back in token order
   shared     (variant) S shared experts that every token passes through with weight 1,
              added after the routed slots
+  bf16       (variant) the whole layer in bfloat16: x, weights and the intermediate (the
+             activation rounded once to bfloat16), no scales
 
 Sources (pages of the study, cited by title and section):
   * "fix(sm90): support parameterized SwiGLU in FP8 MegaMoE" (DeepGEMM PR #445),
@@ -322,6 +324,16 @@ def expert_rows(d, inputs, e: int, tokens: np.ndarray):
     Returns (h codes [n, I], h scales [n, I/128], Y2 float64 [n, H]).
     """
     H, I, fmt = d.hidden, d.inter, d.weight_format
+    if fmt == "bf16":
+        # BF16 layer: operands are bfloat16 bit patterns, no scales; h is the activation's
+        # float32 value rounded once to bfloat16 (nearest even); h_sf is not produced (zeros)
+        bf = lambda a: decode_bf16(a).astype(np.float64)
+        x = bf(inputs["x"][tokens])
+        gu = x @ bf(inputs["w1"][e]).T
+        h = activation(gu[:, :I], gu[:, I:], d.activation, d.act_clamp, d.act_alpha, d.act_up_bias)
+        hq = bf16_rne_bits(h.astype(np.float32).astype(np.float64))
+        hs = np.zeros((hq.shape[0], I // 128), np.uint8)
+        return hq, hs, bf(hq) @ bf(inputs["w2"][e]).T
     if getattr(d, "scaling", "block") == "tensor":
         # per-tensor: every scale is one float32 (x: [1], weights: one per expert), the
         # intermediate uses the descriptor's static h_scale; h_sf is not produced (zeros)
@@ -381,7 +393,7 @@ def layer_tokens(d, inputs, tokens=None):
     want = np.zeros(T, dtype=bool)
     want[toks] = True
     y2 = np.zeros((max(NR, 1), d.hidden), dtype=np.float64)
-    h = np.zeros((max(NR, 1), d.inter), dtype=np.uint8)
+    h = np.zeros((max(NR, 1), d.inter), dtype=np.uint16 if d.weight_format == "bf16" else np.uint8)
     h_sf = np.zeros((max(NR, 1), d.inter // 128), dtype=np.uint8)
     h_valid = np.zeros(max(NR, 1), dtype=bool)
     for e in range(E_loc):

@@ -129,6 +129,18 @@ def topk_bruteforce(logits_row, k):
     return ids, ls
 
 
+def bf16_decode_torch(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 through torch's bfloat16 dtype."""
+    return torch.from_numpy(np.ascontiguousarray(bits).astype(np.uint16).view(np.int16)).view(torch.bfloat16) \
+        .to(torch.float64).numpy()
+
+
+def bf16_round_torch(h32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns by torch's cast (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(h32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
 def requant_tensor_row(h: np.ndarray, h_scale: float):
     """float32 row -> E4M3 codes of h / h_scale (exact rational quotient, saturated at 448)."""
     s = Fraction(float(np.float32(h_scale)))
@@ -144,15 +156,22 @@ def layer_bruteforce(d, inputs):
     """Token-by-token dense evaluation: y[t] = sum_j w_tj * FFN_{e_tj}(x_t), float64."""
     T, H, I, k = d.tokens, d.hidden, d.inter, d.topk
     tensor = getattr(d, "scaling", "block") == "tensor"
+    bf16 = d.weight_format == "bf16"
     S = getattr(d, "num_shared", 0)
     NE = d.num_local + S  # weight sets: routed local experts, then shared experts
     xs = np.zeros((T, H))
-    xv = decode_e4m3_torch(inputs["x"])
-    for t in range(T):
-        for c in range(H):
-            s = float(inputs["x_sf"][0]) if tensor else 2.0 ** (int(inputs["x_sf"][t, c // 128]) - 127)
-            xs[t, c] = xv[t, c] * s
-    if tensor:
+    if bf16:
+        xs = bf16_decode_torch(inputs["x"])
+    else:
+        xv = decode_e4m3_torch(inputs["x"])
+        for t in range(T):
+            for c in range(H):
+                s = float(inputs["x_sf"][0]) if tensor else 2.0 ** (int(inputs["x_sf"][t, c // 128]) - 127)
+                xs[t, c] = xv[t, c] * s
+    if bf16:
+        w1 = [bf16_decode_torch(inputs["w1"][e]) for e in range(NE)]
+        w2 = [bf16_decode_torch(inputs["w2"][e]) for e in range(NE)]
+    elif tensor:
         dec = decode_e4m3_torch if d.weight_format == "fp8" else decode_e5m2_torch
         w1 = [dec(inputs["w1"][e]) * float(inputs["w1_sf"][e]) for e in range(NE)]
         w2 = [dec(inputs["w2"][e]) * float(inputs["w2_sf"][e]) for e in range(NE)]
@@ -174,7 +193,9 @@ def layer_bruteforce(d, inputs):
             u = np.array([sum(xs[t, c] * w1[le][I + n, c] for c in range(H)) for n in range(I)])
             h = np.array([act_scalar(g[n], u[n], d.activation, d.act_clamp, d.act_alpha, d.act_up_bias)
                           for n in range(I)], dtype=np.float32)
-            if tensor:
+            if bf16:
+                hd = bf16_decode_torch(bf16_round_torch(h))
+            elif tensor:
                 hq = requant_tensor_row(h, d.h_scale)
                 hd = np.array([decode_e4m3_torch(hq[n:n + 1])[0] * float(np.float32(d.h_scale)) for n in range(I)])
             else:

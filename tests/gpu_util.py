@@ -15,7 +15,9 @@ def say(msg: str):
 
 
 def upload(inp):
-    return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in inp.items()}
+    # bfloat16 bit patterns travel as int16 (same bytes)
+    return {k: torch.from_numpy(np.ascontiguousarray(v.view(np.int16) if v.dtype == np.uint16 else v)).cuda()
+            for k, v in inp.items()}
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -61,15 +63,19 @@ def run_split(w, dev, variant=-1):
     B.moe_route_permute(d, dev["logits"], ids, tw, counts, offsets, r2s, s2r, ws)
     h = torch.empty((T * (k + S), I), dtype=torch.uint8, device="cuda")  # routed rows, then shared
     tensor = getattr(w, "scaling", "block") == "tensor"
-    h_sf = None if tensor else torch.empty((T * (k + S), I // 128), dtype=torch.uint8, device="cuda")
+    bf16 = w.weight_format == "bf16"
+    if bf16:  # h holds bfloat16 values; no scales
+        h = torch.empty((T * (k + S), I), dtype=torch.int16, device="cuda")
+    h_sf = None if tensor or bf16 else torch.empty((T * (k + S), I // 128), dtype=torch.uint8, device="cuda")
     B.moe_grouped_fc1_swiglu(d, dev["x"], dev["x_sf"], dev["w1"], dev["w1_sf"], offsets, r2s, h, h_sf, ws)
     y = torch.empty((T, w.hidden), dtype=torch.int16, device="cuda")
     B.moe_grouped_fc2_combine(d, h, h_sf, dev["w2"], dev["w2_sf"], offsets, r2s, s2r, tw, y, ws)
     torch.cuda.synchronize()
     R = int(offsets[-1].item())
     NR = R + S * T
-    hs = np.zeros((NR, I // 128), np.uint8) if tensor else h_sf[:NR].cpu().numpy()
-    return {"y_bf16": y.cpu().numpy().view(np.uint16), "h": h[:NR].cpu().numpy(), "h_sf": hs,
+    hs = np.zeros((NR, I // 128), np.uint8) if tensor or bf16 else h_sf[:NR].cpu().numpy()
+    hh = h[:NR].cpu().numpy()
+    return {"y_bf16": y.cpu().numpy().view(np.uint16), "h": hh.view(np.uint16) if bf16 else hh, "h_sf": hs,
             "R": R, "offsets": offsets.cpu().numpy(), "row_to_slot": r2s.cpu().numpy(),
             "slot_to_row": s2r.cpu().numpy(), "topk_ids": ids.cpu().numpy(), "topk_w": tw.cpu().numpy(),
             "counts": counts.cpu().numpy()}
@@ -87,6 +93,7 @@ def check_routing(got, ref, R=None):
 
 
 FP8_RANGE_EPS = 3e-5
+BF16_ROW_EPS = 1e-5
 
 
 def _e4m3_value(c: np.ndarray) -> np.ndarray:
@@ -107,6 +114,20 @@ def h_agreement(gh, ghs, rh, rhs, valid=None):
     """
     if valid is not None:
         gh, ghs, rh, rhs = gh[valid], ghs[valid], rh[valid], rhs[valid]
+    if gh.dtype == np.uint16:
+        # BF16 intermediate: equal, or one bfloat16 step (of the larger magnitude) apart plus
+        # the accumulation error, taken as BF16_ROW_EPS of the row's largest magnitude
+        a, b = bf16_to_f64(gh), bf16_to_f64(rh)
+        big = np.maximum(np.abs(a), np.abs(b))
+        _, ex = np.frexp(big)
+        step = np.ldexp(1.0, ex - 8)
+        floor = BF16_ROW_EPS * np.abs(b).max(axis=-1, keepdims=True) if b.size else 0.0
+        bad = np.abs(a - b) > step + floor
+        if bad.any():
+            rr, cc = np.nonzero(bad)
+            detail = [(int(r), int(c), float(a[r, c]), float(b[r, c])) for r, c in zip(rr[:8], cc[:8])]
+            raise AssertionError(f"{int(bad.sum())} bfloat16 intermediate values differ by more than one step: {detail}")
+        return (float((gh == rh).mean()) if gh.size else 1.0), 1.0
     sf_eq = float((ghs == rhs).mean()) if ghs.size else 1.0
     same_sf = np.repeat(ghs == rhs, 128, axis=1)
     eq = (gh == rh) | (((gh & 0x7F) == 0) & ((rh & 0x7F) == 0))

@@ -31,7 +31,8 @@ def _sample_tokens(ref, w, n=12, seed=0):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["decode", "decode/fp8e5m2", "decode/shared1", "prefill_zipf", "mxfp4_large"])
+@pytest.mark.parametrize("name", ["decode", "decode/fp8e5m2", "decode/shared1", "decode/bf16", "prefill_zipf",
+                                  "mxfp4_large"])
 def test_fullsize_sampled_parity(name):
     """The fused layer at full size.  Workloads of at most 256 tokens are checked on every
     token, larger ones on a seeded sample.

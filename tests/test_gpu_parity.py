@@ -51,6 +51,11 @@ def _small_cases():
                                     num_local=8, topk=4, num_shared=1, seed=18)),
         ("shared2_partial", synth.shrink(tiny, tokens=40, hidden=512, inter=256, num_experts=64, local_begin=10,
                                          num_local=8, topk=4, num_shared=2, seed=19)),
+        # the whole layer in bfloat16 (x, weights, h), with a shared expert in the second case
+        ("bf16_oai", synth.shrink(oai, tokens=300, hidden=768, inter=384, num_experts=16, local_begin=2,
+                                  num_local=8, topk=4, weight_format="bf16", seed=25)),
+        ("bf16_shared", synth.shrink(tiny, tokens=100, hidden=512, inter=256, num_experts=32, num_local=8, topk=4,
+                                     weight_format="bf16", num_shared=1, seed=26)),
         ("top1", synth.shrink(tiny, tokens=130, topk=1, seed=11)),
         ("k16_e1024", synth.shrink(tiny, tokens=40, num_experts=1024, local_begin=1000, num_local=24, topk=16,
                                    seed=12)),
@@ -92,7 +97,7 @@ def test_layer_parity_small(name, w):
 
 @pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("name", ["ragged_oai", "ragged_h384_share", "zipf_small", "mxfp4_small", "e5m2_small",
-                                  "tensor_oai", "shared_oai", "k16_e1024"])
+                                  "tensor_oai", "shared_oai", "bf16_oai", "k16_e1024"])
 def test_layer_parity_forced_variant(name, variant):
     w = dict(_small_cases())[name]
     G.say(f"[variant] {name} variant={variant}")

@@ -215,3 +215,34 @@ def test_shared_expert_equals_routing_every_token_to_it():
     assert np.all(only_shared["topk_w"] == 1.0)
     routed = O.layer(synth.shrink(d, num_shared=0), {k: (v[:4] if k.startswith("w") else v) for k, v in inp.items()})
     assert np.allclose(out["y64"], routed["y64"] + only_shared["y64"], rtol=0, atol=1e-12 * np.abs(out["y64"]).max())
+
+
+@pytest.mark.parametrize("d", [
+    _tiny(weight_format="bf16", seed=41),
+    _tiny(weight_format="bf16", activation="swigluoai", act_clamp=7.0, act_alpha=1.702, act_up_bias=1.0,
+          num_shared=1, seed=42),
+])
+def test_bf16_layer_matches_token_by_token_bruteforce(d):
+    inp = synth.generate(d)
+    assert inp["x"].dtype == np.uint16 and inp["w1"].dtype == np.uint16
+    out = O.layer(d, inp)
+    ref = brute.layer_bruteforce(d, inp)
+    err = np.abs(out["y64"] - ref).max() / max(np.abs(ref).max(), 1e-30)
+    assert err < 1e-12
+    assert np.array_equal(out["y_bf16"], O.bf16_rne_bits(ref))
+
+
+def test_bf16_intermediate_is_one_rounding_of_the_activation():
+    """h of the BF16 layer equals torch's bfloat16 cast of the float32 activation of the
+    float64 gate/up products (computed here from torch's bfloat16 decode of the operands)."""
+    d = _tiny(weight_format="bf16", tokens=8, seed=43)
+    inp = synth.generate(d)
+    out = O.layer(d, inp)
+    e = 0
+    rows = np.arange(out["offsets"][e], out["offsets"][e + 1])
+    toks = out["row_to_slot"][rows] // d.topk
+    x = brute.bf16_decode_torch(inp["x"][toks])
+    gu = x @ brute.bf16_decode_torch(inp["w1"][e]).T
+    g, u = gu[:, :d.inter], gu[:, d.inter:]
+    h = (g / (1 + np.exp(-g)) * u).astype(np.float32)
+    assert np.array_equal(out["h"][rows], brute.bf16_round_torch(h))
