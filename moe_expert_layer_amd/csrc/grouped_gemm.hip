@@ -642,6 +642,7 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   // amax of each row: over the lane's values (an unsigned max of the non-negative float
   // bits), then with lane l ^ 32 (the other half of the columns), then across the WN waves
   // through LDS.  Both lanes of a pair write the same value to the same place.
+  uint32_t rmax[C::MI];
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
     uint32_t m = 0;
@@ -653,9 +654,14 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
         m = m > v ? m : v;
       }
     const uint32_t o = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)m);
-    s_amax[wn][trow + mi * 32] = __uint_as_float(m > o ? m : o);
+    rmax[mi] = m > o ? m : o;
   }
-  __syncthreads();  // every wave is past its last ring read; s_amax complete
+  // s_amax lies inside the ring, possibly in the stage the slowest wave still reads: write
+  // it once every wave is past its last ring read
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) s_amax[wn][trow + mi * 32] = __uint_as_float(rmax[mi]);
+  __syncthreads();  // s_amax complete
   // E4M3 codes, four consecutive columns per dword (two packed conversions), into the
   // [BM rows][128 B] code tile with its 16-byte chunks XOR-swizzled by row (the rows of one
   // wave's writes then spread over the banks); the UE8M0 byte of each row goes to a [BM]
