@@ -94,7 +94,11 @@ def make_desc(num_tokens: int, hidden: int, inter: int, num_experts: int, topk: 
               activation_clamp: Optional[float] = None, activation_alpha: float = 1.0,
               activation_up_bias: float = 0.0, variant: int = -1, scaling: str = "block",
               h_scale: float = 1.0, num_shared: int = 0) -> MoeLayerDesc:
-    """Descriptor with the pages' keyword names (activation, activation_clamp/alpha/up_bias)."""
+    """Descriptor with the pages' keyword names (activation, activation_clamp/alpha/up_bias).
+
+    weight_format: "fp8" (E4M3), "fp8e5m2", "mxfp4" or "bf16" (the whole layer in BF16);
+    scaling: "block" (UE8M0 scale tensors) or "tensor" (float32 scales, static h_scale);
+    num_shared: shared experts after the local ones in the weight tensors."""
     d = MoeLayerDesc()
     _check(lib().moe_desc_defaults(ctypes.byref(d)))
     d.num_tokens, d.hidden, d.inter = num_tokens, hidden, inter

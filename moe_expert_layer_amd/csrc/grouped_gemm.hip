@@ -1,9 +1,12 @@
-// Grouped expert GEMMs on gfx950 scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).
+// Grouped expert GEMMs on gfx950 scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), or BF16
+// MFMA (v_mfma_f32_32x32x16_bf16) for the BF16 layer.
 //
 // FC1: for every row r of local expert e (token t = row_to_slot[r] / k)
 //        g = x_t . W1[e, n],  u = x_t . W1[e, I + n]   (FP8 E4M3 x with 1x128 UE8M0 scales,
-//        W1 FP8 E4M3 with 128x128 UE8M0 scales or MXFP4 with 1x32 UE8M0 scales)
-//      then SwiGLU / OAI-SwiGLU and the 1x128 requant to E4M3 + UE8M0 (fused epilogue).
+//        W1 FP8 E4M3 or E5M2 with 128x128 UE8M0 scales or MXFP4 with 1x32 UE8M0 scales;
+//        per-tensor: one float32 scale for x and one per expert)
+//      then SwiGLU / OAI-SwiGLU and the 1x128 requant to E4M3 + UE8M0 (fused epilogue;
+//      per-tensor: E4M3 of h / h_scale, saturated; BF16 layer: h rounded to BF16).
 // FC2: Y2[r, m] = h_r . W2[e, m]  (fp32 rows kept for the combine).
 // Shared experts (applied to every token) follow the routed local experts: shared expert s
 // owns rows [R + s T, R + (s + 1) T), row R + s T + t being token t.

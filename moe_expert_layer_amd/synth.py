@@ -1,13 +1,15 @@
 """Seeded synthetic inputs for the MoE expert layer.
 
 This module only *makes inputs*: routing logits, FP8 E4M3 activations with 1x128
-UE8M0 scales, and expert weights as FP8 E4M3 with 128x128 UE8M0 block scales or
-as MXFP4 (E2M1 nibbles with one UE8M0 scale per 32 elements).  It holds none of
+UE8M0 scales, and expert weights as FP8 E4M3 (or E5M2) with 128x128 UE8M0 block
+scales or as MXFP4 (E2M1 nibbles with one UE8M0 scale per 32 elements); variants
+with one float32 scale per tensor, with shared experts, or all in BF16.  It holds none of
 the layer's arithmetic (routing, grouping, GEMMs, activation, requantisation,
 combine); both the HIP path and the CPU oracle consume the bytes it returns.
 
 Encodings of the produced bytes (what both consumers must assume):
-  * E4M3 is the OCP 8-bit "E4M3FN" format (bias 7, max 448, no inf).
+  * E4M3 is the OCP 8-bit "E4M3FN" format (bias 7, max 448, no inf); E5M2 is OCP
+    E5M2 (bias 15, max 57344).  BF16 values are bit patterns (uint16).
   * UE8M0 byte b means 2**(b - 127).
   * MXFP4: element 2i of a K-row sits in the low nibble of byte i, element 2i+1 in
     the high nibble; nibble = sign<<3 | exp<<1 | mantissa (E2M1, bias 1).
