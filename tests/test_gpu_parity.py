@@ -191,9 +191,16 @@ def test_zero_tokens_noop():
     torch.cuda.synchronize()
 
 
-def test_graph_capture_replay():
+def _graph_cases():
+    oai = synth.shrink(synth.workload("oai"), tokens=256, hidden=512, inter=256, seed=24)
+    return [("fp8", oai),
+            ("tensor_shared", synth.tensor_scaled(synth.shrink(oai, num_shared=1, seed=27))),
+            ("bf16", synth.shrink(oai, weight_format="bf16", seed=28))]
+
+
+@pytest.mark.parametrize("name,w", _graph_cases(), ids=[c[0] for c in _graph_cases()])
+def test_graph_capture_replay(name, w):
     """moe_layer captured in a HIP graph replays to the eager result every time."""
-    w = synth.shrink(synth.workload("oai"), tokens=256, hidden=512, inter=256, seed=24)
     inp = synth.generate(w)
     dev = G.upload(inp)
     eager = G.run_layer(w, dev)
@@ -217,3 +224,17 @@ def test_graph_capture_replay():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().view(np.uint16), eager["y_bf16"]), f"replay {i}"
+
+
+def test_zero_shared_expert_leaves_routed_output_bit_exact():
+    """A shared expert whose W2 is all zero adds exactly +0 to every token: the output equals
+    the layer without shared experts bit for bit (and the routed rows are unaffected)."""
+    w = synth.shrink(synth.workload("oai"), tokens=200, hidden=512, inter=256, num_experts=16, num_local=8,
+                     topk=4, num_shared=1, seed=29)
+    inp = synth.generate(w)
+    inp["w2"][w.num_local:] = 0
+    with_shared = G.run_layer(w, G.upload(inp))
+    w0 = synth.shrink(w, num_shared=0)
+    inp0 = {k: (v[:w.num_local] if k in ("w1", "w1_sf", "w2", "w2_sf") else v) for k, v in inp.items()}
+    without = G.run_layer(w0, G.upload(inp0))
+    assert np.array_equal(with_shared["y_bf16"], without["y_bf16"])
