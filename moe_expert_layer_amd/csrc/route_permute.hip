@@ -242,18 +242,42 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __re
   __shared__ int wcnt[16][kPermSmallBuckets];
   const int NB = EL + 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the bucket of each of this thread's slots (slot r * 1024 + tid of round r), loaded once
+  // and kept for the scatter; -1 past the last slot
+  constexpr int kRounds = kPermSmallSlots / 1024;
+  const int nrounds = (nslots + 1023) / 1024;
+  int bk[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int s = r * 1024 + tid;
+    bk[r] = s < nslots ? bucket_of(ids[s], e0, EL) : -1;
+  }
   for (int i = tid; i < 2048; i += 1024) a[i] = mt[i] = 0;
   for (int i = tid; i < 16 * kPermSmallBuckets; i += 1024) (&wcnt[0][0])[i] = 0;
   __syncthreads();
-  for (int s = tid; s < nslots; s += 1024) atomicAdd(&a[bucket_of(ids[s], e0, EL)], 1);
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    if (bk[r] >= 0) atomicAdd(&a[bk[r]], 1);
   __syncthreads();
   for (int b = tid; b < EL; b += 1024) {
     counts[b] = a[b];
     mt[b] = (a[b] + bm - 1) / bm;
   }
   __syncthreads();
-  block_exclusive_scan_2048(a);
-  block_exclusive_scan_2048(mt);
+  if (NB <= 64) {  // one wave scans both (entries past NB are zero and stay unused)
+    if (wave == 0) {
+      const int v = lane < NB ? a[lane] : 0, m = lane < NB ? mt[lane] : 0;
+      const int iv = wave_inclusive_scan(v), im = wave_inclusive_scan(m);
+      if (lane < NB) {
+        a[lane] = iv - v;
+        mt[lane] = im - m;
+      }
+    }
+    __syncthreads();
+  } else {
+    block_exclusive_scan_2048(a);
+    block_exclusive_scan_2048(mt);
+  }
   for (int b = tid; b < NB; b += 1024) {
     offsets[b] = a[b];
     plan[b] = mt[b];
@@ -263,10 +287,12 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __re
   int nbits = 1;
   while ((1 << nbits) < NB) ++nbits;
   const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int r0 = 0; r0 < nslots; r0 += 1024) {
-    const int s = r0 + tid;
-    const bool valid = s < nslots;
-    const int b = valid ? bucket_of(ids[s], e0, EL) : 0;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    if (r >= nrounds) break;  // uniform
+    const int s = r * 1024 + tid;
+    const bool valid = bk[r] >= 0;
+    const int b = valid ? bk[r] : 0;
     uint64_t match = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool on = (b >> bit) & 1;

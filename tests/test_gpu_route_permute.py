@@ -1,0 +1,49 @@
+"""GPU routing and grouping against the oracle, bit for bit, across the permute's code paths:
+the one-workgroup permute with a one-wave bucket scan (at most 63 local experts), with the
+block scan (64 to 256 local experts), several rounds of 1024 slots, and the chunked
+multi-workgroup permute (more than 16384 slots or more than 256 local experts)."""
+import numpy as np
+import pytest
+
+from moe_expert_layer_amd import synth
+from oracle import moe_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import gpu_util as G
+    from moe_expert_layer_amd import binding as B
+
+CASES = [  # tokens, experts, local_begin, local, topk
+    (100, 64, 0, 63, 4),      # 64 buckets: one-wave scan, boundary
+    (100, 128, 10, 64, 4),    # 65 buckets: block scan, boundary
+    (700, 256, 0, 256, 8),    # 257 buckets: largest one-workgroup case, several rounds
+    (2048, 64, 3, 40, 8),     # 16384 slots exactly: sixteen rounds
+    (2049, 64, 3, 40, 8),     # one slot more: chunked permute
+    (64, 1024, 500, 300, 16), # 301 buckets: chunked permute
+    (1, 8, 0, 8, 1),          # a single slot
+]
+
+
+@pytest.mark.parametrize("T,E,e0,EL,k", CASES)
+def test_route_permute_bit_exact(T, E, e0, EL, k):
+    G.say(f"[route] T={T} E={E} e0={e0} EL={EL} k={k}")
+    rng = np.random.default_rng(T * 7 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, ::5] = np.round(logits[:, ::5])  # exact ties
+    w = synth.shrink(synth.workload("tiny"), tokens=T, num_experts=E, local_begin=e0, num_local=EL, topk=k)
+    d = B.desc_from_workload(w)
+    ws = B.alloc_workspace(d)
+    i32 = lambda *s: torch.empty(s, dtype=torch.int32, device="cuda")
+    ids, tw = i32(T, k), torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts, offsets, r2s, s2r = i32(EL), i32(EL + 1), i32(T * k), i32(T * k)
+    r2s.fill_(-7)
+    B.moe_route_permute(d, torch.from_numpy(logits).cuda(), ids, tw, counts, offsets, r2s, s2r, ws)
+    torch.cuda.synchronize()
+    rid, rw = O.route(logits, k)
+    rc, ro, rr, rs = O.permute(rid, e0, EL)
+    got = {"topk_ids": ids.cpu().numpy(), "topk_w": tw.cpu().numpy(), "counts": counts.cpu().numpy(),
+           "offsets": offsets.cpu().numpy(), "row_to_slot": r2s.cpu().numpy(), "slot_to_row": s2r.cpu().numpy()}
+    G.check_routing(got, {"topk_ids": rid, "topk_w": rw, "counts": rc, "offsets": ro, "row_to_slot": rr,
+                          "slot_to_row": rs})
