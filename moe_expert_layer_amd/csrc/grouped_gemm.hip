@@ -146,7 +146,10 @@ struct Frags {
 
 // the source is a uniform 64-bit base plus a 32-bit per-lane offset (the saddr form); the base
 // is passed through readfirstlane so it sits in SGPRs even where the compiler cannot prove it
-// uniform
+// uniform.  A VMEM instruction that reads an SGPR written by a VALU instruction (readfirstlane,
+// an SGPR spill reload) needs 5 wait states in between; the compiler inserts them before its
+// own loads but not inside inline asm, so the asm provides them: s_mov + s_nop 3 (this also
+// covers the 1 wait state between writing m0 and the LDS DMA that reads it)
 __device__ __forceinline__ const void* sbase(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
@@ -154,12 +157,12 @@ __device__ __forceinline__ const void* sbase(const void* p) {
 }
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
   base = sbase(base);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
   base = sbase(base);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 template <int N>
