@@ -65,6 +65,15 @@ def _small_cases():
         # more than 256 local experts: chunked permute as well
         ("many_local", synth.shrink(tiny, tokens=96, hidden=256, inter=128, num_experts=1024, local_begin=100,
                                     num_local=300, topk=8, seed=14)),
+        # the largest contraction the kernels take (K = 8192: 64 scale steps staged in LDS),
+        # in FC1 (hidden) and in FC2 (intermediate)
+        ("max_k_fc1", synth.shrink(tiny, tokens=40, hidden=8192, inter=256, num_experts=4, num_local=4, topk=2,
+                                   seed=29)),
+        ("max_k_fc2", synth.shrink(tiny, tokens=40, hidden=256, inter=8192, num_experts=4, num_local=4, topk=2,
+                                   seed=30)),
+        # every token routed to every expert (k = E); a share of one expert
+        ("k_equals_e", synth.shrink(tiny, tokens=50, num_experts=4, num_local=4, topk=4, seed=31)),
+        ("one_local", synth.shrink(tiny, tokens=70, num_experts=16, local_begin=15, num_local=1, topk=3, seed=32)),
     ]
 
 
@@ -97,7 +106,7 @@ def test_layer_parity_small(name, w):
 
 @pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("name", ["ragged_oai", "ragged_h384_share", "zipf_small", "mxfp4_small", "e5m2_small",
-                                  "tensor_oai", "shared_oai", "bf16_oai", "k16_e1024"])
+                                  "tensor_oai", "shared_oai", "bf16_oai", "k16_e1024", "max_k_fc1", "max_k_fc2"])
 def test_layer_parity_forced_variant(name, variant):
     w = dict(_small_cases())[name]
     G.say(f"[variant] {name} variant={variant}")
@@ -189,6 +198,24 @@ def test_zero_tokens_noop():
     e = torch.empty(0, dtype=torch.uint8, device="cuda")
     B.moe_layer(d, e, e, e, e, e, e, e, y, ws)
     torch.cuda.synchronize()
+
+
+def test_no_local_rows_gives_zero_output():
+    """Routing that never picks a local expert: no rows, both GEMMs have no tiles, and y is
+    exactly zero (the oracle agrees bit for bit)."""
+    w = synth.shrink(synth.workload("tiny"), tokens=90, num_experts=16, local_begin=4, num_local=6, topk=3,
+                     seed=33)
+    inp = synth.generate(w)
+    logits = inp["logits"].copy()
+    logits[:, w.local_begin:w.local_begin + w.num_local] = -1e30  # finite, below every other logit
+    inp["logits"] = logits
+    ref = O.layer(w, inp)
+    assert not (ref["slot_to_row"] >= 0).any()
+    dev = G.upload(inp)
+    for got in (G.run_split(w, dev), G.run_layer(w, dev)):
+        G.check_routing(got, ref)
+        assert got.get("R", 0) == 0
+        assert np.all(got["y_bf16"] == 0) and np.array_equal(got["y_bf16"], ref["y_bf16"])
 
 
 def _graph_cases():
