@@ -18,6 +18,20 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Inclusive sum over the wave with DPP: shifts by 1, 2, 4, 8 inside each 16-lane row
+// (lanes whose source is outside the row add 0), then the last lane of row 0 and row 2 is
+// added to rows 1 and 3 (row_bcast:15) and the last lane of row 1 to rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return v;
+}
+
 // Exclusive scan of a[0..2048) (in LDS) by a 1024-thread workgroup; a[] must be
 // complete and visible (barrier) on entry.  Ends with a barrier.
 __device__ __forceinline__ void block_exclusive_scan_2048(int* a) {

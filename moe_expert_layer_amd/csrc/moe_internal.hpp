@@ -10,6 +10,8 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 16;
 constexpr int kMaxShared = 4;  // shared experts per layer
 constexpr int kPermChunk = 4096;  // slots per permute workgroup
+constexpr int kPermTinySlots = 8192;    // at most this many slots and ...
+constexpr int kPermTinyBuckets = 64;    // ... 63 local experts: the one-workgroup permute without atomics
 constexpr int kPermSmallSlots = 16384;  // at most this many slots: one-workgroup permute
 constexpr int kPermSmallBuckets = 257;  // ... and at most 256 local experts
 

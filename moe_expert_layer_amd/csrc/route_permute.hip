@@ -327,10 +327,97 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __re
   }
 }
 
+// One workgroup, no atomics (up to 8192 slots, up to 63 local experts): the slots form
+// chunks of 64 in slot order (round r of wave w is chunk 16 r + w).  Each wave ranks its
+// slots among the equal buckets of its chunk with ballots and one lane per bucket stores
+// the chunk's count; a wave per bucket turns the counts into exclusive prefixes over the
+// chunks; one wave scans the bucket totals.  Position of a slot = bucket offset + prefix of
+// its chunk + rank: stable by slot id.
+__global__ __launch_bounds__(1024) void permute_tiny_kernel(const int32_t* __restrict__ ids, int nslots, int e0,
+                                                            int EL, int bm, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ row_to_slot,
+                                                            int32_t* __restrict__ slot_to_row,
+                                                            int32_t* __restrict__ plan) {
+  constexpr int kChunks = kPermTinySlots / 64;
+  constexpr int kRounds = kPermTinySlots / 1024;
+  __shared__ int cnt[kPermTinyBuckets][kChunks];  // [bucket][chunk]: count, then prefix
+  __shared__ int base[kPermTinyBuckets];
+  const int NB = EL + 1;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nrounds = (nslots + 1023) / 1024, nchunks = (nslots + 63) / 64;
+  int bk[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int s = r * 1024 + tid;
+    bk[r] = s < nslots ? bucket_of(ids[s], e0, EL) : -1;
+  }
+  for (int i = tid; i < kPermTinyBuckets * kChunks; i += 1024) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  int nbits = 1;
+  while ((1 << nbits) < NB) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  int rank[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    rank[r] = 0;
+    if (r >= nrounds) continue;  // uniform
+    const bool valid = bk[r] >= 0;
+    const int b = valid ? bk[r] : 0;
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (b >> bit) & 1;
+      const uint64_t m = __ballot(valid && on);
+      match &= on ? m : ~m;
+    }
+    rank[r] = __popcll(match & lt);
+    if (valid && rank[r] == 0) cnt[b][r * 16 + wave] = __popcll(match);
+  }
+  __syncthreads();
+  for (int b = wave; b < NB; b += 16) {
+    int carry = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {  // uniform
+      const int c = c0 + lane;
+      const int v = c < nchunks ? cnt[b][c] : 0;
+      const int inc = wave_inclusive_scan_dpp(v);
+      if (c < nchunks) cnt[b][c] = carry + inc - v;
+      carry += __builtin_amdgcn_readlane(inc, 63);
+    }
+    if (lane == 0) base[b] = carry;  // bucket total
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int v = lane < NB ? base[lane] : 0;
+    const int m = lane < EL ? (v + bm - 1) / bm : 0;  // m-tiles of this expert
+    const int iv = wave_inclusive_scan_dpp(v), im = wave_inclusive_scan_dpp(m);
+    if (lane < NB) {
+      offsets[lane] = iv - v;
+      plan[lane] = im - m;
+      base[lane] = iv - v;
+    }
+    if (lane < EL) counts[lane] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    if (r >= nrounds) break;  // uniform
+    const int b = bk[r];
+    if (b < 0) continue;
+    const int s = r * 1024 + tid;
+    const int pos = base[b] + cnt[b][r * 16 + wave] + rank[r];
+    row_to_slot[pos] = b < EL ? s : -1;
+    slot_to_row[s] = b < EL ? pos : -1;
+  }
+}
+
 hipError_t launch_permute(const int32_t* ids, int nslots, int e0, int EL, int32_t* chunk_cnt, int32_t* chunk_base,
                           int32_t* counts, int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row, int bm,
                           int32_t* plan, hipStream_t s) {
   const int NB = EL + 1;
+  if (nslots <= kPermTinySlots && NB <= kPermTinyBuckets) {
+    permute_tiny_kernel<<<1, 1024, 0, s>>>(ids, nslots, e0, EL, bm, counts, offsets, row_to_slot, slot_to_row, plan);
+    return hipGetLastError();
+  }
   if (nslots <= kPermSmallSlots && NB <= kPermSmallBuckets) {
     permute_small_kernel<<<1, 1024, 0, s>>>(ids, nslots, e0, EL, bm, counts, offsets, row_to_slot, slot_to_row, plan);
     return hipGetLastError();
