@@ -1,7 +1,9 @@
 """GPU routing and grouping against the oracle, bit for bit, across the permute's code paths:
-the one-workgroup permute with a one-wave bucket scan (at most 63 local experts), with the
-block scan (64 to 256 local experts), several rounds of 1024 slots, and the chunked
-multi-workgroup permute (more than 16384 slots or more than 256 local experts)."""
+the atomic-free one-workgroup permute (at most 8192 slots and 63 local experts; chunk
+prefixes over one or two wave-wide passes), the one-workgroup permute with a one-wave
+bucket scan (more slots, at most 63 local experts) or the block scan (64 to 256 local
+experts), several rounds of 1024 slots, and the chunked multi-workgroup permute (more than
+16384 slots or more than 256 local experts)."""
 import numpy as np
 import pytest
 
@@ -16,7 +18,10 @@ if torch.cuda.is_available():
     from moe_expert_layer_amd import binding as B
 
 CASES = [  # tokens, experts, local_begin, local, topk
-    (100, 64, 0, 63, 4),      # 64 buckets: one-wave scan, boundary
+    (100, 64, 0, 63, 4),      # 64 buckets: atomic-free permute, bucket boundary
+    (600, 64, 5, 50, 8),      # 4800 slots = 75 chunks: the chunk prefix carries into a second pass
+    (1024, 64, 3, 40, 8),     # 8192 slots = 128 chunks: largest atomic-free case
+    (1025, 64, 3, 40, 8),     # 8200 slots: one-workgroup permute with the one-wave bucket scan
     (100, 128, 10, 64, 4),    # 65 buckets: block scan, boundary
     (700, 256, 0, 256, 8),    # 257 buckets: largest one-workgroup case, several rounds
     (2048, 64, 3, 40, 8),     # 16384 slots exactly: sixteen rounds
