@@ -275,7 +275,6 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* d, const uint8_t* x, con
     return fail(MOE_ERR_MISALIGNED, "x / x_sf / w1 / w1_sf / h not 16-byte aligned");
   if (moe_status st = check_ws(d, ws, ws_bytes)) return st;
   if (moe_status st = check_device()) return st;
-  const Layout L = make_layout(*d);
   const moe::Shape sh = shape_of(*d);
   MOE_TRY_HIP(moe::launch_fc1(sh, pick_variant(*d), x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
                               nullptr, false, (hipStream_t)stream));
