@@ -561,8 +561,10 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
   if (MODE == 2) {
     // ---- FC2 epilogue (tokens are the MFMA's first operand: lane l of acc[mi][ct] holds
     //      rows 8*(i/4) + 4*kb + i%4 of row tile mi, column bcol(ct) + l%32): fp32 rows of Y2,
-    //      32 consecutive columns per lane group, stored non-temporally so the burst at the
-    //      end of the tiles does not evict the operands ----
+    //      32 consecutive columns per lane group.  The 256-row tiles (shares with hundreds of
+    //      MB of Y2) store non-temporally so the burst at the end of the tiles does not evict
+    //      the operands; the smaller tiles' Y2 (tens of MB) stays in the caches for the
+    //      combine, which reads it next ----
     if (wave_live) {
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi)
@@ -574,7 +576,10 @@ __global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kerne
 #pragma unroll
             for (int ct = 0; ct < C::NT; ++ct) {
               const int col = n0 + bcol(ct) + lrow;
-              if (col < g.N) __builtin_nontemporal_store(acc[mi][ct][i], dst + col);  // read once, by the combine
+              if (col < g.N) {
+                if constexpr (BM == 256) __builtin_nontemporal_store(acc[mi][ct][i], dst + col);
+                else dst[col] = acc[mi][ct][i];
+              }
             }
           }
         }
