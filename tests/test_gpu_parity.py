@@ -265,3 +265,32 @@ def test_zero_shared_expert_leaves_routed_output_bit_exact():
     inp0 = {k: (v[:w.num_local] if k in ("w1", "w1_sf", "w2", "w2_sf") else v) for k, v in inp.items()}
     without = G.run_layer(w0, G.upload(inp0))
     assert np.array_equal(with_shared["y_bf16"], without["y_bf16"])
+
+
+def test_concurrent_streams_with_distinct_workspaces():
+    """Layers on two streams at once, each with its own workspace (the header allows this):
+    every result equals the same layer run alone, bit for bit."""
+    from moe_expert_layer_amd import binding as B
+    cases = [synth.shrink(synth.workload("oai"), tokens=400, hidden=1024, inter=512, num_experts=16, num_local=8,
+                          topk=4, seed=34),
+             synth.shrink(synth.workload("tiny"), tokens=300, hidden=768, inter=256, num_experts=24, local_begin=3,
+                          num_local=9, topk=5, seed=35, weight_format="mxfp4")]
+    runs = []
+    for w in cases:
+        dev = G.upload(synth.generate(w))
+        alone = G.run_layer(w, dev)["y_bf16"]
+        d = B.desc_from_workload(w)
+        ws = B.alloc_workspace(d)
+        ys = [torch.empty((w.tokens, w.hidden), dtype=torch.int16, device="cuda") for _ in range(3)]
+        runs.append((w, dev, d, ws, ys, alone))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    torch.cuda.synchronize()
+    for it in range(3):  # three layer calls per stream, interleaved at issue
+        for (w, dev, d, ws, ys, _), st in zip(runs, streams):
+            with torch.cuda.stream(st):
+                B.moe_layer(d, dev["logits"], dev["x"], dev["x_sf"], dev["w1"], dev["w1_sf"], dev["w2"],
+                            dev["w2_sf"], ys[it], ws, stream=st)
+    torch.cuda.synchronize()
+    for w, dev, d, ws, ys, alone in runs:
+        for y in ys:
+            assert np.array_equal(y.cpu().numpy().view(np.uint16), alone)
