@@ -1,9 +1,11 @@
-"""GPU routing and grouping against the oracle, bit for bit, across the permute's code paths:
+"""GPU routing and grouping against the oracle, bit for bit, across the routing kernels (one
+wave per token; one 16-lane row per token from 16384 tokens) and the permute's code paths:
 the atomic-free one-workgroup permute (at most 8192 slots and 63 local experts; chunk
 prefixes over one or two wave-wide passes), the one-workgroup permute with a one-wave
 bucket scan (more slots, at most 63 local experts) or the block scan (64 to 256 local
 experts), several rounds of 1024 slots, and the chunked multi-workgroup permute (more than
-16384 slots or more than 256 local experts)."""
+16384 slots or more than 256 local experts; ballot-ranked chunks for at most 63 local
+experts, more than 64 chunks in one case)."""
 import numpy as np
 import pytest
 
@@ -27,6 +29,11 @@ CASES = [  # tokens, experts, local_begin, local, topk
     (2048, 64, 3, 40, 8),     # 16384 slots exactly: sixteen rounds
     (2049, 64, 3, 40, 8),     # one slot more: chunked permute
     (64, 1024, 500, 300, 16), # 301 buckets: chunked permute
+    (33000, 64, 3, 40, 8),    # 264000 slots = 65 chunks: the chunk scan carries into a second pass
+    # 16384 tokens or more: routing with one 16-lane row per token (1, 2 and 8 keys per lane)
+    (16384, 16, 0, 16, 4),
+    (16400, 32, 0, 20, 3),
+    (16384, 100, 10, 40, 16),
     (1, 8, 0, 8, 1),          # a single slot
 ]
 
