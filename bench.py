@@ -103,8 +103,8 @@ def main():
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU expert-parallel "
-              "exchange is not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library computes one GPU's "
+              "expert share, and the expert-parallel exchange across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

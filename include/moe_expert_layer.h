@@ -104,7 +104,7 @@ typedef enum {
   MOE_ERR_NULL = 1,          /* a required pointer is NULL */
   MOE_ERR_INVALID_DESC = 2,  /* a size or parameter in the descriptor is out of range */
   MOE_ERR_MISALIGNED = 3,    /* a pointer violates the alignment rules above */
-  MOE_ERR_UNSUPPORTED = 4,   /* valid request this build cannot run (e.g. not a gfx950 device) */
+  MOE_ERR_UNSUPPORTED = 4,   /* valid request the library cannot run (e.g. not a gfx950 device) */
   MOE_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than moe_workspace_size() */
   MOE_ERR_DEVICE = 6         /* a HIP runtime call or launch failed */
 } moe_status;
