@@ -32,11 +32,12 @@
 // E4M3 packing then stay mostly inside the lane); FC2 keeps tokens first (row-contiguous
 // Y2 stores).
 //
-// Tiles: 128 rows x BN weight rows (FC1: BN = 256 = 128 gate + the matching 128 up rows,
-// i.e. exactly one 1x128 requant block of h; FC2: BN output columns), 4 waves in 2x2.
-// K advances 128 per stage through a ring of NSTAGE LDS stages filled by direct
-// global->LDS loads (global_load_lds_dwordx4): NSTAGE-1 stages are in flight while one is
-// consumed, and the loads take no registers.  The waits are explicit (s_waitcnt vmcnt +
+// Tiles: BM rows x BN weight rows (FC1: BN = 256 = 128 gate + the matching 128 up rows,
+// i.e. exactly one 1x128 requant block of h; FC2: BN output columns), in three variants:
+// 128 rows with 4 waves (2 x 2), 256 rows with 8 waves (4 x 2) and 32 rows with 4 waves
+// (1 x 4).  K advances BK bytes per stage through a ring of NSTAGE LDS stages filled by
+// direct global->LDS loads (global_load_lds_dwordx4): NSTAGE-1 stages are in flight while
+// one is consumed, and the loads take no registers.  The waits are explicit (s_waitcnt vmcnt +
 // s_barrier).  LDS rows are 16-byte-chunk XOR swizzled so the operand reads are bank
 // conflict free.  Workgroups map to tiles in an XCD-aware order (consecutive tiles of one
 // expert on one XCD, sharing its L2).  Waves whose rows all lie past an expert's last row
