@@ -193,8 +193,14 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ plan, int
   return lo;
 }
 
+// Two workgroups per CU for the tiles whose ring fits twice in LDS (the register budget
+// follows from that); one otherwise.
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
-__global__ __launch_bounds__(NW * 64, BM <= 128 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
+constexpr int kWgPerCu = NSTAGE * Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>::STAGE <= 80 * 1024 ? 2 : 1;
+
+template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
+__global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>)) void grouped_gemm_kernel(
+    GemmArgs g) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   using F = Frags<C::MI, C::NT, C::NH>;
   // LDS (dynamic, sized at launch): the stage ring, then the tile's activation scales
@@ -772,11 +778,13 @@ static hipError_t launch_variant_w(const GemmArgs& a, int variant, size_t grid, 
     if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 32, 256, 128, 3, 4, 32, 2>(a, grid, s);
     else return launch_one<MODE, WFMT, 32, 256, 128, 2, 4, 32, 2>(a, grid, s);
   }
-  // small experts: two workgroups fit one CU (<= 80 KB of LDS each) so one streams weights
-  // while the other is in its prologue or epilogue; FC2 tiles are 128 columns wide
+  // experts with tens of rows: FC2 tiles are 128 columns wide, two workgroups per CU (one
+  // streams weights while the other is in its prologue or epilogue); FC1 streams whole
+  // 128-byte weight-row segments through a three-stage ring (one workgroup per CU), except
+  // MXFP4, whose 64-byte stages keep two workgroups per CU
   if constexpr (MODE == 2) return launch_one<MODE, WFMT, 128, 128, 128, 2, 4, 64, 0>(a, grid, s);
   else if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 128, 256, 64, 4, 4, 64, 0>(a, grid, s);
-  else return launch_one<MODE, WFMT, 128, 256, 64, 3, 4, 64, 0>(a, grid, s);
+  else return launch_one<MODE, WFMT, 128, 256, 128, 3, 4, 64, 0>(a, grid, s);
 }
 
 // weight formats: 0 FP8 E4M3 with 128x128 scales, 1 MXFP4, 2 FP8 E5M2 with 128x128 scales,
