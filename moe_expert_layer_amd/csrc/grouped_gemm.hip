@@ -784,13 +784,14 @@ static hipError_t launch_variant_w(const GemmArgs& a, int variant, size_t grid, 
     if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 32, 256, 128, 3, 4, 32, 2>(a, grid, s);
     else return launch_one<MODE, WFMT, 32, 256, 128, 2, 4, 32, 2>(a, grid, s);
   }
-  // experts with tens of rows: FC2 tiles are 128 columns wide, two workgroups per CU (one
-  // streams weights while the other is in its prologue or epilogue); FC1 streams whole
-  // 128-byte weight-row segments through a three-stage ring (one workgroup per CU), except
-  // MXFP4, whose 64-byte stages keep two workgroups per CU
-  if constexpr (MODE == 2) return launch_one<MODE, WFMT, 128, 128, 128, 2, 4, 64, 0>(a, grid, s);
+  // experts with tens of rows: FC2 tiles are 128 columns wide, two workgroups of 8 waves
+  // per CU (one streams weights while the other is in its prologue or epilogue); FC1 streams
+  // whole 128-byte weight-row segments through a three-stage ring, one workgroup of 8 waves
+  // per CU (two per SIMD, so one wave's LDS reads overlap the other's MFMAs), except MXFP4,
+  // whose 64-byte stages keep two workgroups per CU
+  if constexpr (MODE == 2) return launch_one<MODE, WFMT, 128, 128, 128, 2, 8, 32, 0>(a, grid, s);
   else if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 128, 256, 64, 4, 4, 64, 0>(a, grid, s);
-  else return launch_one<MODE, WFMT, 128, 256, 128, 3, 4, 64, 0>(a, grid, s);
+  else return launch_one<MODE, WFMT, 128, 256, 128, 3, 8, 32, 0>(a, grid, s);
 }
 
 // weight formats: 0 FP8 E4M3 with 128x128 scales, 1 MXFP4, 2 FP8 E5M2 with 128x128 scales,
