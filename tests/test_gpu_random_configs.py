@@ -13,6 +13,8 @@ Checks, for the three-call path and the one-call entry point:
   a single requantisation flip, itself within one grid step, can move a tiny layer's norm
   by more than the bar).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -26,7 +28,7 @@ if torch.cuda.is_available():
     from tests import gpu_util as G
 
 TOL = 2e-3
-N_CASES = 32
+N_CASES = int(os.environ.get("MOE_RANDOM_CASES", "32"))  # a longer sweep: MOE_RANDOM_CASES=300
 
 
 def random_case(i: int):
