@@ -32,6 +32,20 @@ def _run(bits):
     return x.cpu().numpy(), sf.cpu().numpy()
 
 
+def _ties():
+    """Blocks whose largest magnitude is 448 (scale byte 127: codes are the values rounded
+    directly) filled with every midpoint between adjacent positive E4M3 values, normal and
+    subnormal, with both signs: round-to-nearest-even decides each one (all are exact in bf16)."""
+    grid = np.sort(np.unique(np.abs(O.decode_e4m3(np.arange(256, dtype=np.uint8)))))
+    grid = grid[np.isfinite(grid)]
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([mids, -mids])
+    n = -(-len(vals) // 127) * 127
+    vals = np.concatenate([vals, np.zeros(n - len(vals))]).reshape(-1, 127)
+    blocks = np.concatenate([np.full((len(vals), 1), 448.0), vals], 1)  # one block per row
+    return blocks.astype(np.float32)
+
+
 def _cases():
     rng = np.random.default_rng(40)
     n = lambda *s: rng.standard_normal(s).astype(np.float32)
@@ -39,7 +53,8 @@ def _cases():
                               np.concatenate([np.zeros((1, 128)), n(1, 128)], 1)]).astype(np.float32)
     return [("n01_1x128", n(1, 128)), ("n01_37x384", n(37, 384)), ("n01_300x2048", n(300, 2048)),
             ("cauchy_129x7168", rng.standard_cauchy((129, 7168)).astype(np.float32)),
-            ("tiny_8x1024", n(8, 1024) * 1e-30), ("large_8x1024", n(8, 1024) * 1e30), ("special", special)]
+            ("tiny_8x1024", n(8, 1024) * 1e-30), ("large_8x1024", n(8, 1024) * 1e30), ("special", special),
+            ("e4m3_ties", _ties())]
 
 
 @pytest.mark.parametrize("name,v", _cases(), ids=[c[0] for c in _cases()])
