@@ -253,6 +253,50 @@ def test_graph_capture_replay(name, w):
         assert np.array_equal(y.cpu().numpy().view(np.uint16), eager["y_bf16"]), f"replay {i}"
 
 
+@pytest.mark.parametrize("name,w", [
+    ("oai", synth.shrink(synth.workload("oai"), tokens=256, hidden=512, inter=256, seed=36)),
+    # 16800 slots: the chunked permute (histogram, chunk scan, scatter) inside the graph
+    ("chunked", synth.shrink(synth.workload("tiny"), tokens=2100, hidden=256, inter=128, num_experts=64,
+                             num_local=16, topk=8, seed=37))], ids=["oai", "chunked"])
+def test_graph_capture_replay_split_calls(name, w):
+    """The three split calls (route/permute, FC1, FC2 + combine) captured in one HIP graph
+    replay to the eager result every time, with the workspace poisoned between replays."""
+    from moe_expert_layer_amd import binding as B
+    dev = G.upload(synth.generate(w))
+    eager = G.run_split(w, dev)
+    d = B.desc_from_workload(w)
+    ws = B.alloc_workspace(d)
+    T, k, EL, I = w.tokens, w.topk, w.num_local, w.inter
+    ids, tw = G.i32(T, k), torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts, offsets, r2s, s2r = G.i32(EL), G.i32(EL + 1), G.i32(T * k), G.i32(T * k)
+    h = torch.empty((T * k, I), dtype=torch.uint8, device="cuda")
+    h_sf = torch.empty((T * k, I // 128), dtype=torch.uint8, device="cuda")
+    y = torch.zeros((T, w.hidden), dtype=torch.int16, device="cuda")
+
+    def calls():
+        B.moe_route_permute(d, dev["logits"], ids, tw, counts, offsets, r2s, s2r, ws)
+        B.moe_grouped_fc1_swiglu(d, dev["x"], dev["x_sf"], dev["w1"], dev["w1_sf"], offsets, r2s, h, h_sf, ws)
+        B.moe_grouped_fc2_combine(d, h, h_sf, dev["w2"], dev["w2_sf"], offsets, r2s, s2r, tw, y, ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for i in range(3):
+        y.zero_()
+        ws.fill_(0xAB)  # poison the workspace between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), eager["y_bf16"]), f"{name} replay {i}"
+        assert np.array_equal(offsets.cpu().numpy(), eager["offsets"]), f"{name} replay {i}"
+
+
 def test_zero_shared_expert_leaves_routed_output_bit_exact():
     """A shared expert whose W2 is all zero adds exactly +0 to every token: the output equals
     the layer without shared experts bit for bit (and the routed rows are unaffected)."""
