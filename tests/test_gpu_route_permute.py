@@ -35,6 +35,12 @@ CASES = [  # tokens, experts, local_begin, local, topk
     (16400, 32, 0, 20, 3),
     (16384, 100, 10, 40, 16),
     (1, 8, 0, 8, 1),          # a single slot
+    (512, 32, 0, 32, 4),      # the oai share's routing shape
+    (1024, 8, 0, 8, 8),       # every expert taken
+    (257, 33, 1, 30, 5),      # expert count not a multiple of 4
+    (256, 64, 0, 63, 16),     # largest k
+    (128, 256, 0, 32, 8),     # the decode share's routing shape
+    (1000, 16, 0, 16, 8),
 ]
 
 
