@@ -68,11 +68,14 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
   const float* row = logits + (size_t)t * E;
+  float v[VPL];  // every load unconditional (index clamped), so all are in flight at once
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
   uint64_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? route_key(row[e], e) : 0ull;
+    key[i] = e < E ? route_key(v[i], e) : 0ull;
   }
   uint64_t mine = 0;  // lane j: the key of slot j
   for (int j = 0; j < k; ++j) {
@@ -114,11 +117,14 @@ __global__ __launch_bounds__(256) void route_topk_row_kernel(const float* __rest
   const int t = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
   const bool valid = t < T;
   const float* row = logits + (size_t)(valid ? t : 0) * E;
+  float v[NK];  // every load unconditional (index clamped), so all are in flight at once
+#pragma unroll
+  for (int i = 0; i < NK; ++i) v[i] = row[min(lr + 16 * i, E - 1)];
   uint64_t key[NK];
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
     const int e = lr + 16 * i;
-    key[i] = valid && e < E ? route_key(row[e], e) : 0ull;
+    key[i] = valid && e < E ? route_key(v[i], e) : 0ull;
   }
   uint64_t mine = 0, first = 0;  // lane j of the row: the key of slot j; every lane: slot 0's
   for (int j = 0; j < k; ++j) {
@@ -190,6 +196,12 @@ __device__ __forceinline__ int bucket_of(int id, int e0, int EL) {
   return (le >= 0 && le < EL) ? le : EL;  // EL = the non-local bucket
 }
 
+// ids[s], or ids[n - 1] past the end (n >= 1): the load is unconditional, so a run of them
+// is in flight together instead of each waiting behind a branch of its own
+__device__ __forceinline__ int load_clamped(const int32_t* __restrict__ ids, int s, int n) {
+  return ids[s < n ? s : n - 1];
+}
+
 // Per-chunk bucket histogram (order-free integer counts).
 __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ ids, int nslots, int e0, int EL,
                                                            int32_t* __restrict__ chunk_cnt) {
@@ -198,10 +210,13 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
   for (int b = threadIdx.x; b < NB; b += 256) hist[b] = 0;
   __syncthreads();
   const int base = blockIdx.x * kPermChunk;
-  for (int i = threadIdx.x; i < kPermChunk; i += 256) {
-    const int s = base + i;
-    if (s < nslots) atomicAdd(&hist[bucket_of(ids[s], e0, EL)], 1);
-  }
+  constexpr int kPer = kPermChunk / 256;
+  int id[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) id[r] = load_clamped(ids, base + r * 256 + (int)threadIdx.x, nslots);
+#pragma unroll
+  for (int r = 0; r < kPer; ++r)
+    if (base + r * 256 + (int)threadIdx.x < nslots) atomicAdd(&hist[bucket_of(id[r], e0, EL)], 1);
   __syncthreads();
   for (int b = threadIdx.x; b < NB; b += 256) chunk_cnt[(size_t)blockIdx.x * NB + b] = hist[b];
 }
@@ -323,7 +338,8 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __re
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int s = r * 1024 + tid;
-    bk[r] = s < nslots ? bucket_of(ids[s], e0, EL) : -1;
+    const int id = load_clamped(ids, s, nslots);
+    bk[r] = s < nslots ? bucket_of(id, e0, EL) : -1;
   }
   for (int i = tid; i < 2048; i += 1024) a[i] = mt[i] = 0;
   for (int i = tid; i < 16 * kPermSmallBuckets; i += 1024) (&wcnt[0][0])[i] = 0;
@@ -423,7 +439,8 @@ __global__ __launch_bounds__(1024) void permute_tiny_kernel(const int32_t* __res
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int s = r * 1024 + tid;
-    bk[r] = s < nslots ? bucket_of(ids[s], e0, EL) : -1;
+    const int id = load_clamped(ids, s, nslots);
+    bk[r] = s < nslots ? bucket_of(id, e0, EL) : -1;
   }
   for (int i = tid; i < kPermTinyBuckets * kChunks; i += 1024) (&cnt[0][0])[i] = 0;
   __syncthreads();
@@ -507,7 +524,8 @@ __global__ __launch_bounds__(256) void permute_scatter64_kernel(const int32_t* _
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int s = first + r * 256 + tid;
-    bk[r] = s < nslots ? bucket_of(ids[s], e0, EL) : -1;
+    const int id = load_clamped(ids, s, nslots);
+    bk[r] = s < nslots ? bucket_of(id, e0, EL) : -1;
   }
   __syncthreads();
   int nbits = 1;
