@@ -216,11 +216,18 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
 
   // tile plan: plan[e] = m-tiles of the experts before e, plan[EL] = all.  The fused path
   // passes the one the permute wrote; the split entry points pass none and every workgroup
-  // scans the offsets itself (into the ring, which the prologue does not use yet)
-  const int32_t* plan = g.plan;
-  if (plan == nullptr) {
-    int* s_plan = reinterpret_cast<int*>(ring);  // [EL + 1]
-    int* s_wsum = s_plan + kMaxExperts + 8;      // [NW]
+  // scans the offsets itself.  Either way the plan and the expert offsets are put in LDS
+  // (inside the ring, which the prologue does not use yet) by loads that are all in flight
+  // together, so the expert search below reads LDS instead of chaining dependent global loads
+  int* s_plan = reinterpret_cast<int*>(ring);  // [EL + S + 1]
+  int* s_wsum = s_plan + kMaxExperts + 8;      // [NW]
+  int* s_offs = s_wsum + 16;                   // [EL + 1]
+  static_assert(NSTAGE * C::STAGE >= (2 * kMaxExperts + 32) * 4 + BM * 4, "plan and offsets fit before s_tok");
+  for (int j = threadIdx.x; j <= g.EL; j += C::NTHR) s_offs[j] = g.offsets[j];
+  if (g.plan != nullptr) {
+    for (int j = threadIdx.x; j <= g.EL + g.S; j += C::NTHR) s_plan[j] = g.plan[j];
+    __syncthreads();
+  } else {
     const int t = threadIdx.x, n = g.EL + g.S + 1, per = (n + C::NTHR - 1) / C::NTHR, beg = t * per;
     int sum = 0;
     for (int j = 0; j < per; ++j) {
@@ -237,8 +244,8 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     for (int j = 0; j < per; ++j)
       if (beg + j < n) s_plan[beg + j] += base;
     __syncthreads();
-    plan = s_plan;
   }
+  const int* plan = s_plan;
   const int NE = g.EL + g.S;  // experts with rows: routed, then shared
   const int total = plan[NE] * g.n_tiles;
   const int bid = blockIdx.x;
@@ -259,8 +266,8 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   const int n_tile = grp * gn + idx % gsz;
   // rows of expert e: routed experts from the offsets, shared expert s = e - EL after them
   const bool shared = e >= g.EL;
-  const int seg_begin = shared ? g.offsets[g.EL] + (e - g.EL) * g.T : g.offsets[e];
-  const int seg_end = shared ? seg_begin + g.T : g.offsets[e + 1];
+  const int seg_begin = shared ? s_offs[g.EL] + (e - g.EL) * g.T : s_offs[e];
+  const int seg_end = shared ? seg_begin + g.T : s_offs[e + 1];
   const int row_begin = seg_begin + m_tile * BM;
   const int rows = min(BM, seg_end - row_begin);
 
