@@ -288,7 +288,9 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     s_tok[i] = MODE == 2 ? row_begin + r : shared ? row_begin + r - seg_begin : g.row_to_slot[row_begin + r] / g.k;
   }
   // FP8 weight scales of the tile's two 128-row blocks (FC1: gate n0/128 and up (I+n0)/128;
-  // FC2: n0/128 and n0/128 + 1, clamped), loaded now and written to LDS after the DMA issue
+  // FC2: n0/128 and n0/128 + 1, clamped), loaded now and written to LDS before the first DMA:
+  // the compiler cannot count the DMAs (inline asm), so its wait for this load is a full
+  // vmcnt(0) and, placed after them, would drain every stage in flight
   const uint8_t* bsf_e = g.B_sf + (long long)e * g.bsf_estride;
   const bool bsf_mine = WFMT != 1 && !C::BF16 && tid < 2 * nk128;
   int bsf_v = 0;
@@ -349,6 +351,10 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   uint32_t s_off = 0;
   if (WFMT == 1) s_off = (uint32_t)b_row((wave % (BN / 64)) * 64 + lane) * (uint32_t)(g.K / 32);
   __syncthreads();  // s_tok (inside the ring) is consumed before the ring is filled
+  if (bsf_mine) s_bsf[tid] = (uint8_t)bsf_v;  // before any DMA; published by the first wait's barrier
+  // every wave, scale lanes or not: no load of the compiler's own is outstanding past this
+  // point, so it adds no vmcnt(0) (which would also drain the DMAs) for this load's register
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited for
   if (asf_dma) {
 #pragma unroll
     for (int j = 0; j < kAsfDma; ++j)
@@ -496,11 +502,10 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     else if (C::MI > 3 && live_tiles == 3) mma_n(f, std::integral_constant<int, (C::MI > 3 ? 3 : 1)>{});
   };
 
-  // prologue: NSTAGE-1 stages in flight (the first wait's barrier also publishes s_bsf)
+  // prologue: NSTAGE-1 stages in flight
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < nk) issue(s);
-  if (bsf_mine) s_bsf[tid] = (uint8_t)bsf_v;
 
   if (PIPE == 0) {
     for (int ks = 0; ks < nk; ++ks) {
