@@ -223,11 +223,15 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   int* s_wsum = s_plan + kMaxExperts + 8;      // [NW]
   int* s_offs = s_wsum + 16;                   // [EL + 1]
   static_assert(NSTAGE * C::STAGE >= (2 * kMaxExperts + 32) * 4 + BM * 4, "plan and offsets fit before s_tok");
-  for (int j = threadIdx.x; j <= g.EL; j += C::NTHR) s_offs[j] = g.offsets[j];
-  if (g.plan != nullptr) {
-    for (int j = threadIdx.x; j <= g.EL + g.S; j += C::NTHR) s_plan[j] = g.plan[j];
+  if (g.plan != nullptr) {  // no shared experts on this path: the plan has EL + 1 entries
+    for (int j = threadIdx.x; j <= g.EL; j += C::NTHR) {
+      const int o = g.offsets[j], p = g.plan[j];  // both loads in flight before either store
+      s_offs[j] = o;
+      s_plan[j] = p;
+    }
     __syncthreads();
   } else {
+    for (int j = threadIdx.x; j <= g.EL; j += C::NTHR) s_offs[j] = g.offsets[j];
     const int t = threadIdx.x, n = g.EL + g.S + 1, per = (n + C::NTHR - 1) / C::NTHR, beg = t * per;
     int sum = 0;
     for (int j = 0; j < per; ++j) {
