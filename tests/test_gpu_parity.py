@@ -74,6 +74,10 @@ def _small_cases():
         # every token routed to every expert (k = E); a share of one expert
         ("k_equals_e", synth.shrink(tiny, tokens=50, num_experts=4, num_local=4, topk=4, seed=31)),
         ("one_local", synth.shrink(tiny, tokens=70, num_experts=16, local_begin=15, num_local=1, topk=3, seed=32)),
+        # the most local experts (1024): the GEMM prologue's plan and offsets in LDS fill
+        # their whole regions over several passes of the workgroup's threads
+        ("max_local", synth.shrink(tiny, tokens=64, hidden=256, inter=128, num_experts=1024, num_local=1024,
+                                   topk=4, seed=33)),
     ]
 
 
@@ -106,13 +110,18 @@ def test_layer_parity_small(name, w):
 
 @pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("name", ["ragged_oai", "ragged_h384_share", "zipf_small", "mxfp4_small", "e5m2_small",
-                                  "tensor_oai", "shared_oai", "bf16_oai", "k16_e1024", "max_k_fc1", "max_k_fc2"])
+                                  "tensor_oai", "shared_oai", "bf16_oai", "k16_e1024", "max_k_fc1", "max_k_fc2",
+                                  "max_local"])
 def test_layer_parity_forced_variant(name, variant):
+    """Each tile shape against the oracle (three-call path, whose GEMMs derive the tile plan
+    themselves), and the one-call entry point (the permute's plan) bit-identical to it."""
     w = dict(_small_cases())[name]
     G.say(f"[variant] {name} variant={variant}")
     inp = synth.generate(w)
     ref = O.layer(w, inp)
-    got = G.run_split(w, G.upload(inp), variant=variant)
+    dev = G.upload(inp)
+    got = G.run_split(w, dev, variant=variant)
+    assert np.array_equal(G.run_layer(w, dev, variant=variant)["y_bf16"], got["y_bf16"])
     G.check_routing(got, ref)
     be, se = G.h_agreement(got["h"], got["h_sf"], ref["h"], ref["h_sf"])
     err = G.rel_fro(G.bf16_to_f64(got["y_bf16"]), G.bf16_to_f64(ref["y_bf16"]))
