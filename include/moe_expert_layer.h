@@ -160,11 +160,25 @@ const char* moe_last_error(void);
 moe_status moe_desc_defaults(moe_layer_desc* desc);
 
 /* Bytes of workspace every entry point below needs for this descriptor.  Host only;
- * validates the descriptor. */
+ * validates the descriptor.  The pages split the fused layer's API into a buffer-sizing /
+ * allocation call and the execution calls ("fix(sm90): support parameterized SwiGLU in FP8
+ * MegaMoE", Changes: buffer allocation and execution APIs), and build the layer as
+ * config -> buffer -> compute ("Pull Style Cutedsl Megakernel", Layout); here the caller
+ * owns the buffer and this call sizes it.
+ * Errors: MOE_ERR_NULL (desc or bytes NULL), MOE_ERR_INVALID_DESC, MOE_ERR_UNSUPPORTED. */
 moe_status moe_workspace_size(const moe_layer_desc* desc, size_t* bytes);
 
 /* Route + permute: logits -> topk_ids, topk_w, counts, offsets, row_to_slot, slot_to_row.
- * All outputs are required (caller-owned device buffers of the sizes above). */
+ * All outputs are required (caller-owned device buffers of the sizes above).
+ * The fused layer consumes tokens grouped by expert (the grouped, "masked/unmasked" expert
+ * layouts of "Optimize sm100 version with token-aware BM240 tiling, native UE8M0, and direct
+ * combine", description) and its top-k reduce needs each token's k expert ids and weights
+ * ("Pull Style Cutedsl Megakernel", Layout: topk_reduce).  The pages do not define the
+ * routing function; this call takes the top k logits (ties to the lower expert id) and a
+ * float64 softmax over those k, rounded once to float32.  Grouping is stable in the slot id
+ * s = t*k + j, so the result is unique.  Reads logits [T, E_tot]; writes every output;
+ * uses the workspace for its histograms.  Errors: MOE_ERR_NULL, MOE_ERR_MISALIGNED,
+ * MOE_ERR_WORKSPACE, MOE_ERR_INVALID_DESC, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
 moe_status moe_route_permute(const moe_layer_desc* desc, const float* logits, int32_t* topk_ids,
                              float* topk_w, int32_t* counts, int32_t* offsets, int32_t* row_to_slot,
                              int32_t* slot_to_row, void* workspace, size_t workspace_bytes,
@@ -172,7 +186,16 @@ moe_status moe_route_permute(const moe_layer_desc* desc, const float* logits, in
 
 /* FC1 + activation + 1x128 requant for every row of every local expert.
  * Reads x/x_sf rows of token row_to_slot[r] / k (shared expert rows: every token in
- * order), writes h/h_sf rows [0, R + S*T). */
+ * order), writes h/h_sf rows [0, R + S*T).
+ * Sources: the gate/up GEMM with the activation applied in its epilogue, standard SwiGLU or
+ * OAI-SwiGLU with clamp / alpha / up_bias ("fix(sm90): support parameterized SwiGLU in FP8
+ * MegaMoE", Summary and Changes: act_type "swiglu" / "swigluoai"); FP8 operands with native
+ * UE8M0 block scales ("Optimize sm100 version with token-aware BM240 tiling, native UE8M0,
+ * and direct combine", description); the FP8 + 1x128 UE8M0 output emitted from the GEMM
+ * epilogue with an amax per block ("DSV4 o_proj: fuse fp8/UE8M0 quantize into o_a proj",
+ * Description).  offsets and row_to_slot are this call's inputs (from moe_route_permute);
+ * the workspace is not read.  Errors: MOE_ERR_NULL, MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE,
+ * MOE_ERR_INVALID_DESC, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
 moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* desc, const uint8_t* x, const uint8_t* x_sf,
                                   const uint8_t* w1, const uint8_t* w1_sf, const int32_t* offsets,
                                   const int32_t* row_to_slot, uint8_t* h, uint8_t* h_sf,
@@ -181,7 +204,14 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* desc, const uint8_t* x, 
 /* FC2 + top-k weighted combine into y (bf16 bits, [T, H]).  The fp32 FC2 rows are
  * kept in the workspace; the sum over a token's local slots runs in slot order
  * j = 0..k-1 in fp32, then adds the shared experts' rows (weight 1), and is rounded
- * once to bf16.  Reads h/h_sf rows [0, R + S*T). */
+ * once to bf16.  Reads h/h_sf rows [0, R + S*T).
+ * Sources: the fused layer ends FC2 -> top-k reduce ("Pull Style Cutedsl Megakernel",
+ * Layout: fc1_fc2_fuse_sched, topk_reduce), combining each token's expert outputs back into
+ * token order ("Optimize sm100 version with token-aware BM240 tiling, native UE8M0, and
+ * direct combine", description), with run-to-run bitwise-identical outputs (same
+ * description); this reduce has no atomics and a fixed slot order.  Overwrites the whole
+ * of y.  Errors: MOE_ERR_NULL, MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_INVALID_DESC,
+ * MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
 moe_status moe_grouped_fc2_combine(const moe_layer_desc* desc, const uint8_t* h, const uint8_t* h_sf,
                                    const uint8_t* w2, const uint8_t* w2_sf, const int32_t* offsets,
                                    const int32_t* row_to_slot, const int32_t* slot_to_row,
@@ -189,7 +219,13 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* desc, const uint8_t* h,
                                    size_t workspace_bytes, void* stream);
 
 /* The whole layer.  The opt_* outputs may be NULL (then they live in the workspace);
- * when given they receive the routing/grouping results. */
+ * when given they receive the routing/grouping results.
+ * Sources: the fused "Mega MoE" layer, one call from routed tokens to the combined output
+ * ("Pull Style Cutedsl Megakernel", Layout: config -> buffer -> compute, FC1 -> FC2 ->
+ * top-k reduce; "fix(sm90): support parameterized SwiGLU in FP8 MegaMoE", Changes: the
+ * execution API).  Equal bit for bit to moe_route_permute + moe_grouped_fc1_swiglu +
+ * moe_grouped_fc2_combine on the same inputs.  Errors: MOE_ERR_NULL, MOE_ERR_MISALIGNED,
+ * MOE_ERR_WORKSPACE, MOE_ERR_INVALID_DESC, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE. */
 moe_status moe_layer(const moe_layer_desc* desc, const float* logits, const uint8_t* x,
                      const uint8_t* x_sf, const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2,
                      const uint8_t* w2_sf, uint16_t* y, int32_t* opt_topk_ids, float* opt_topk_w,

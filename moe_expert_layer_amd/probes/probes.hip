@@ -1,0 +1,232 @@
+// Measurement probes (not part of the layer): matrix-instruction accumulation precision,
+// matrix-core rate and HBM read bandwidth on gfx950.  The C interface and its conventions
+// are in include/moe_probes.h.
+//
+// Operand layouts used here (gfx950):
+//   scaled 32x32x64 FP8: lane l holds row l%32, K bytes [16*(l/32), +16) and [32 + 16*(l/32), +16)
+//     of the 64-wide step; FP4: K elements [32*(l/32), +32) in its first 16 bytes; result lane l,
+//     value i is row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+//   scaled 16x16x128 FP8: lane l holds row l%16, K bytes [16*(l/16), +16) and [64 + 16*(l/16), +16)
+//     of the 128-wide step; FP4: K elements [32*(l/16), +32); result lane l, value i is row
+//     4*(l/16) + i, column l%16.
+//   32x32x16 FP8 and BF16: lane l holds row l%32, K values [8*(l/32), +8) of the 16-wide step.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "../../include/moe_probes.h"
+
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+__device__ __forceinline__ v8i pair16(uint4 lo, uint4 hi) {
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// E2M1 nibble -> float (OCP MX: sign, 2 exponent bits with bias 1, 1 mantissa bit)
+__device__ __forceinline__ float e2m1(uint32_t nib) {
+  const uint32_t e = (nib >> 1) & 3u, m = nib & 1u;
+  const float mag = e == 0 ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * (float)(1u << (e - 1));
+  return (nib & 8u) ? -mag : mag;
+}
+
+// 8 consecutive K values of a row as BF16 (exact conversions: E4M3 and E2M1 fit BF16)
+__device__ __forceinline__ bf16x8 bf16_of_fp8(uint2 v) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+__device__ __forceinline__ bf16x8 bf16_of_fp4(uint32_t v) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// result of a 32x32 instruction form: lane l, value i -> row 8*(i/4) + 4*(l/32) + i%4, column l%32
+__device__ __forceinline__ void store32(float* c, const v16f& acc, int lane) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[(8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * 32 + (lane & 31)] = acc[i];
+}
+
+template <int BF4>
+__global__ __launch_bounds__(64) void probe_gemm_kernel(int form, int K, const uint8_t* __restrict__ a,
+                                                        const uint8_t* __restrict__ b, float* __restrict__ c) {
+  constexpr bool b_fp4 = BF4 != 0;
+  const int p = blockIdx.x, lane = threadIdx.x;
+  const int bK = b_fp4 ? K / 2 : K;  // bytes per B row
+  const uint8_t* A = a + (long long)p * 32 * K;
+  const uint8_t* Bm = b + (long long)p * 32 * bK;
+  float* C = c + (long long)p * 1024;
+  constexpr int bcode = BF4 ? 4 : 0;  // B operand format of the scaled instructions: E4M3 0, E2M1 4
+
+  if (form == MOE_PROBE_SCALED_32X32X64 || form == MOE_PROBE_SCALED_32X32X64_SPLIT) {
+    const int r = lane & 31, kb = lane >> 5;
+    v16f acc = {};
+    for (int s = 0; s < K / 64; ++s) {
+      const uint8_t* ar = A + r * K + 64 * s;
+      const v8i av = pair16(ld16(ar + 16 * kb), ld16(ar + 32 + 16 * kb));
+      v8i bv;
+      if (b_fp4) {
+        const uint4 q = ld16(Bm + r * bK + 32 * s + 16 * kb);
+        bv = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      } else {
+        const uint8_t* br = Bm + r * bK + 64 * s;
+        bv = pair16(ld16(br + 16 * kb), ld16(br + 32 + 16 * kb));
+      }
+      if (form == MOE_PROBE_SCALED_32X32X64) {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, bcode, 0, 127, 0, 127);
+      } else {
+        const v16f zero = {};
+        const v16f t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, zero, 0, bcode, 0, 127, 0, 127);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += t[i];
+      }
+    }
+    store32(C, acc, lane);
+  } else if (form == MOE_PROBE_SCALED_16X16X128) {
+    const int r = lane & 15, kb = lane >> 4;
+#pragma unroll
+    for (int qm = 0; qm < 2; ++qm)
+#pragma unroll
+      for (int qn = 0; qn < 2; ++qn) {
+        v4f acc = {};
+        for (int s = 0; s < K / 128; ++s) {
+          const uint8_t* ar = A + (16 * qm + r) * K + 128 * s;
+          const v8i av = pair16(ld16(ar + 16 * kb), ld16(ar + 64 + 16 * kb));
+          v8i bv;
+          if (b_fp4) {
+            const uint4 q = ld16(Bm + (16 * qn + r) * bK + 64 * s + 16 * kb);
+            bv = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+          } else {
+            const uint8_t* br = Bm + (16 * qn + r) * bK + 128 * s;
+            bv = pair16(ld16(br + 16 * kb), ld16(br + 64 + 16 * kb));
+          }
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, bcode, 0, 127, 0, 127);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) C[(16 * qm + 4 * (lane >> 4) + i) * 32 + 16 * qn + (lane & 15)] = acc[i];
+      }
+  } else if (form == MOE_PROBE_FP8_32X32X16) {
+    const int r = lane & 31, kb = lane >> 5;
+    v16f acc = {};
+    for (int s = 0; s < K / 16; ++s) {
+      const uint2 av = ld8(A + r * K + 16 * s + 8 * kb);
+      const uint2 bv = ld8(Bm + r * bK + 16 * s + 8 * kb);
+      const long al = (long)(((uint64_t)av.y << 32) | av.x), bl = (long)(((uint64_t)bv.y << 32) | bv.x);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(al, bl, acc, 0, 0, 0);
+    }
+    store32(C, acc, lane);
+  } else if (form == MOE_PROBE_BF16_32X32X16) {
+    const int r = lane & 31, kb = lane >> 5;
+    v16f acc = {};
+    for (int s = 0; s < K / 16; ++s) {
+      const bf16x8 av = bf16_of_fp8(ld8(A + r * K + 16 * s + 8 * kb));
+      const bf16x8 bv = b_fp4 ? bf16_of_fp4(ld4(Bm + r * bK + 8 * s + 4 * kb))
+                              : bf16_of_fp8(ld8(Bm + r * bK + 16 * s + 8 * kb));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+    store32(C, acc, lane);
+  } else if (form == MOE_PROBE_FP32_FMA) {
+    for (int e = lane; e < 1024; e += 64) {
+      const int m = e >> 5, j = e & 31;
+      float acc = 0.f;
+      for (int k = 0; k < K; ++k) {
+        const float av = __builtin_amdgcn_cvt_f32_fp8((int)A[m * K + k], 0);
+        const float bv = b_fp4 ? e2m1((Bm[j * bK + k / 2] >> (4 * (k & 1))) & 15u)
+                               : __builtin_amdgcn_cvt_f32_fp8((int)Bm[j * bK + k], 0);
+        acc = fmaf(av, bv, acc);
+      }
+      C[e] = acc;
+    }
+  }
+}
+
+// Four independent accumulators per wave, operands in registers: the instruction issue rate
+// is the only limit.  The operand bytes are finite FP8 / FP4 values that differ per lane.
+__global__ __launch_bounds__(256) void probe_mfma_loop_kernel(int iters, int b_fp4, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int pat = 0x38383838 ^ ((lane & 7) * 0x01010101);  // E4M3 values near 1
+  const v8i av = v8i{pat, pat, pat, pat, pat, pat, pat, pat};
+  const int fp4pat = 0x22222222 ^ ((lane & 3) * 0x11111111);
+  const v8i bv = b_fp4 ? v8i{fp4pat, fp4pat, fp4pat, fp4pat, 0, 0, 0, 0} : av;
+  v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    if (b_fp4) {
+      c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c0, 0, 4, 0, 120, 0, 120);
+      c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c1, 0, 4, 0, 120, 0, 120);
+      c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c2, 0, 4, 0, 120, 0, 120);
+      c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c3, 0, 4, 0, 120, 0, 120);
+    } else {
+      c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c0, 0, 0, 0, 120, 0, 120);
+      c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c1, 0, 0, 0, 120, 0, 120);
+      c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c2, 0, 0, 0, 120, 0, 120);
+      c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c3, 0, 0, 0, 120, 0, 120);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  sink[(long long)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+typedef int v4i_ __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void probe_hbm_read_kernel(const v4i_* __restrict__ src, long long n16,
+                                                             float* __restrict__ sink) {
+  const long long stride = (long long)gridDim.x * 256;
+  int acc = 0;
+  long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {  // four loads in flight per thread
+    const v4i_ v0 = __builtin_nontemporal_load(src + i);
+    const v4i_ v1 = __builtin_nontemporal_load(src + i + stride);
+    const v4i_ v2 = __builtin_nontemporal_load(src + i + 2 * stride);
+    const v4i_ v3 = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w ^ v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^
+           v3.w;
+  }
+  for (; i < n16; i += stride) {
+    const v4i_ v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[(long long)blockIdx.x * 256 + threadIdx.x] = (float)(acc & 0xffff);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_probe_mfma_gemm(int form, int n, int K, int b_fp4, const uint8_t* a, const uint8_t* b, float* c,
+                        void* stream) {
+  if (form < 0 || form > 5 || n < 1 || n > 65535 || K < 128 || K % 128 || !a || !b || !c) return -1;
+  if (b_fp4 && form == MOE_PROBE_FP8_32X32X16) return -1;
+  if (b_fp4) probe_gemm_kernel<1><<<dim3(n), 64, 0, (hipStream_t)stream>>>(form, K, a, b, c);
+  else probe_gemm_kernel<0><<<dim3(n), 64, 0, (hipStream_t)stream>>>(form, K, a, b, c);
+  return (int)hipGetLastError();
+}
+
+int moe_probe_mfma_loop(int blocks, int iters, int b_fp4, float* sink, void* stream) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20) || !sink) return -1;
+  probe_mfma_loop_kernel<<<dim3(blocks), 256, 0, (hipStream_t)stream>>>(iters, b_fp4 ? 1 : 0, sink);
+  return (int)hipGetLastError();
+}
+
+int moe_probe_hbm_read(const void* src, size_t bytes, int blocks, float* sink, void* stream) {
+  if (blocks < 1 || blocks > (1 << 20) || bytes % 16 || !src || !sink) return -1;
+  probe_hbm_read_kernel<<<dim3(blocks), 256, 0, (hipStream_t)stream>>>(reinterpret_cast<const v4i_*>(src),
+                                                                         (long long)(bytes / 16), sink);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -21,21 +21,27 @@ def L():
     return B.lib()
 
 
-def declared_functions():
-    names = []
-    for fn in os.listdir(os.path.join(ROOT, "include")):
-        if fn.endswith(".h"):
-            src = open(os.path.join(ROOT, "include", fn)).read()
-            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-            names += re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", src, flags=re.M)
-    return sorted(set(names))
+# header -> the library that exports its functions
+HEADERS = {"moe_expert_layer.h": "libmoe_expert_layer.so", "moe_probes.h": "libmoe_probes.so"}
 
 
-def test_exports_every_declared_symbol(L):
-    names = declared_functions()
-    assert len(names) >= 9
+def declared_functions(header):
+    src = open(os.path.join(ROOT, "include", header)).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_header_has_a_library():
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == sorted(HEADERS)
+
+
+@pytest.mark.parametrize("header", sorted(HEADERS))
+def test_exports_every_declared_symbol(L, header):
+    names = declared_functions(header)
+    assert len(names) >= (9 if header == "moe_expert_layer.h" else 3)
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_expert_layer_amd", HEADERS[header]))
     for n in names:
-        assert hasattr(L, n), n
+        assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(L):
@@ -168,3 +174,20 @@ def test_h_sf_optional_only_with_per_tensor_scaling(L):
     d = B.desc_from_workload(synth.tensor_scaled(synth.workload("tiny")))
     # past the pointer checks: the undersized workspace is what is reported
     assert L.moe_grouped_fc1_swiglu(ctypes.byref(d), *args, P(0x100000), 16, None) == B.MOE_ERR_WORKSPACE
+
+
+def test_probe_arguments_rejected_before_launch():
+    """The probe entry points check their arguments on the host (-1) before any launch."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_expert_layer_amd", "libmoe_probes.so"))
+    P = ctypes.c_void_p
+    lib.moe_probe_mfma_gemm.argtypes = [ctypes.c_int] * 4 + [P] * 4
+    lib.moe_probe_mfma_loop.argtypes = [ctypes.c_int] * 3 + [P] * 2
+    lib.moe_probe_hbm_read.argtypes = [P, ctypes.c_size_t, ctypes.c_int, P, P]
+    fake = P(256)  # never dereferenced: every call below fails its argument check
+    assert lib.moe_probe_mfma_gemm(6, 1, 128, 0, fake, fake, fake, None) == -1   # unknown form
+    assert lib.moe_probe_mfma_gemm(0, 0, 128, 0, fake, fake, fake, None) == -1   # no problems
+    assert lib.moe_probe_mfma_gemm(0, 1, 96, 0, fake, fake, fake, None) == -1    # K not a multiple of 128
+    assert lib.moe_probe_mfma_gemm(2, 1, 128, 1, fake, fake, fake, None) == -1   # FP4 with the FP8-only form
+    assert lib.moe_probe_mfma_gemm(0, 1, 128, 0, None, fake, fake, None) == -1   # NULL operand
+    assert lib.moe_probe_mfma_loop(0, 10, 0, fake, None) == -1
+    assert lib.moe_probe_hbm_read(fake, 17, 1, fake, None) == -1                 # not whole 16-byte loads

@@ -1,6 +1,7 @@
 """Full-size workloads on the GPU (the bench's launch configuration: fused moe_layer,
 heuristic kernel variant): routing and grouping bit-exact over every token, layer output
-checked against the oracle on every token (decode sizes) or a seeded sample of tokens."""
+checked against the oracle on every token (decode sizes) or on a seeded sample of tokens
+that reaches every row tile of both grouped GEMMs (larger shares)."""
 import numpy as np
 import pytest
 
@@ -16,8 +17,22 @@ if torch.cuda.is_available():
 TOL = 2e-3
 
 
+BM_LARGE = 256  # row tile of the grouped GEMMs for these shares (the 256-row tile variant)
+
+
+def _tiles(offsets, bm):
+    """(expert, first row, end row) of every row tile of the grouped GEMMs."""
+    out = []
+    for e in range(offsets.size - 1):
+        for r0 in range(int(offsets[e]), int(offsets[e + 1]), bm):
+            out.append((e, r0, min(r0 + bm, int(offsets[e + 1]))))
+    return out
+
+
 def _sample_tokens(ref, w, n=12, seed=0):
-    """Seeded sample: tokens with the most local slots, one with none, the rest random."""
+    """Seeded sample: tokens with the most local slots, one with none, the last token, one
+    token from a random row of every (expert, 256-row tile) of FC1 and FC2 (both GEMMs tile
+    an expert's rows the same way), the rest random."""
     loc = (ref["slot_to_row"].reshape(w.tokens, w.topk) >= 0).sum(1)
     rng = np.random.default_rng(seed)
     pick = set(np.argsort(-loc, kind="stable")[:3].tolist())
@@ -25,9 +40,20 @@ def _sample_tokens(ref, w, n=12, seed=0):
     if none.size:
         pick.add(int(none[0]))
     pick.add(w.tokens - 1)
+    for _, r0, r1 in _tiles(ref["offsets"], BM_LARGE):
+        pick.add(int(ref["row_to_slot"][int(rng.integers(r0, r1))]) // w.topk)
     while len(pick) < n:
         pick.add(int(rng.integers(0, w.tokens)))
     return np.array(sorted(pick))
+
+
+def _tile_coverage(ref, w, toks):
+    """Share of the (expert, 256-row tile) tiles that hold a row of an evaluated token."""
+    row_tok = ref["row_to_slot"][: int(ref["offsets"][-1])] // w.topk
+    ev = np.isin(row_tok, toks)
+    tiles = _tiles(ref["offsets"], BM_LARGE)
+    hit = sum(bool(ev[r0:r1].any()) for _, r0, r1 in tiles)
+    return hit, len(tiles)
 
 
 @pytest.mark.timeout(900)
@@ -61,7 +87,10 @@ def test_fullsize_sampled_parity(name):
     got = G.run_layer(w, dev)
     G.check_routing(got, ref_route)
     toks = np.arange(w.tokens) if w.tokens <= 256 else _sample_tokens(ref_route, w)
-    G.say(f"[fullsize] {name}: oracle on {toks.size} tokens")
+    hit, ntiles = _tile_coverage(ref_route, w, toks)
+    G.say(f"[fullsize] {name}: oracle on {toks.size} tokens; they reach {hit} of {ntiles} "
+          f"(expert, {BM_LARGE}-row tile) tiles ({100.0 * hit / ntiles:.1f}%)")
+    assert hit == ntiles
     ref = O.layer_tokens(w, inp, toks)
     yg = G.bf16_to_f64(got["y_bf16"][toks])
     yr = G.bf16_to_f64(ref["y_bf16"])
