@@ -233,6 +233,30 @@ moe_status moe_layer(const moe_layer_desc* desc, const float* logits, const uint
                      int32_t* opt_slot_to_row, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Size in bytes of the static per-device scratch array that moe_layer_static uses. */
+#define MOE_STATIC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* moe_static_scratch_bytes: MOE_STATIC_SCRATCH_BYTES as built into the loaded library. */
+size_t moe_static_scratch_bytes(void);
+
+/* moe_layer without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as moe_layer, except that the scratch comes from a
+ * static device array of MOE_STATIC_SCRATCH_BYTES (64 MiB) in the library, one per GPU,
+ * held until the process ends; its device address is looked up on the first call on
+ * each device (with that device current).  A layer whose moe_workspace_size exceeds that
+ * size is rejected with MOE_ERR_WORKSPACE before any launch (decode-sized shares fit:
+ * 128 tokens, top-8, hidden 7168, intermediate 2048 need about 33 MB).  The call allocates
+ * nothing and needs no zeroed memory.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other threads) race and give
+ * undefined results; calls ordered on one stream are safe. */
+moe_status moe_layer_static(const moe_layer_desc* desc, const float* logits, const uint8_t* x,
+                            const uint8_t* x_sf, const uint8_t* w1, const uint8_t* w1_sf,
+                            const uint8_t* w2, const uint8_t* w2_sf, uint16_t* y,
+                            int32_t* opt_topk_ids, float* opt_topk_w, int32_t* opt_counts,
+                            int32_t* opt_offsets, int32_t* opt_row_to_slot, int32_t* opt_slot_to_row,
+                            void* stream);
+
 /* Input quantisation (the pages' "DSV4 o_proj: fuse fp8/UE8M0 quantize into o_a proj",
  * Description: FP8 E4M3 with one UE8M0 scale per 1x128 block, from an amax per block).
  * x_bf16 [T, H] bf16 bits -> x [T, H] E4M3 codes and x_sf [T, H/128] UE8M0 bytes, the

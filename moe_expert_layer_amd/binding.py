@@ -70,6 +70,10 @@ def lib():
         L.moe_grouped_fc2_combine.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, VP]
         L.moe_layer.restype = I32
         L.moe_layer.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, VP]
+        L.moe_static_scratch_bytes.restype = ctypes.c_size_t
+        L.moe_static_scratch_bytes.argtypes = []
+        L.moe_layer_static.restype = I32
+        L.moe_layer_static.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, VP]
         L.moe_quantize_act.restype = I32
         L.moe_quantize_act.argtypes = [D, P, P, P, VP]
         L.moe_pack_scales.restype = I32
@@ -165,6 +169,14 @@ def moe_layer(desc, logits, x, x_sf, w1, w1_sf, w2, w2_sf, y, workspace, topk_id
                            _ptr(w2_sf), _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
                            _ptr(row_to_slot), _ptr(slot_to_row), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_layer_static(desc, logits, x, x_sf, w1, w1_sf, w2, w2_sf, y, topk_ids=None, topk_w=None, counts=None,
+                     offsets=None, row_to_slot=None, slot_to_row=None, stream=None):
+    """moe_layer with the library's static scratch array instead of a workspace (allocates nothing)."""
+    _check(lib().moe_layer_static(ctypes.byref(desc), _ptr(logits), _ptr(x), _ptr(x_sf), _ptr(w1), _ptr(w1_sf),
+                                  _ptr(w2), _ptr(w2_sf), _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
+                                  _ptr(offsets), _ptr(row_to_slot), _ptr(slot_to_row), _stream(stream)))
 
 
 def moe_quantize_act(desc, x_bf16, x, x_sf, stream=None):

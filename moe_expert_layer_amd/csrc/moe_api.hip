@@ -304,23 +304,29 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* d, const uint8_t* h, co
   return ok();
 }
 
-moe_status moe_layer(const moe_layer_desc* d, const float* logits, const uint8_t* x, const uint8_t* x_sf,
-                     const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf, uint16_t* y,
-                     int32_t* opt_ids, float* opt_w, int32_t* opt_counts, int32_t* opt_offsets, int32_t* opt_r2s,
-                     int32_t* opt_s2r, void* ws, size_t ws_bytes, void* stream) {
-  if (moe_status st = check_desc(d)) return st;
-  if (d->num_tokens == 0) return ok();
+}  // extern "C"
+
+namespace {
+
+moe_status check_layer_args(const moe_layer_desc* d, const float* logits, const uint8_t* x, const uint8_t* x_sf,
+                            const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf,
+                            const uint16_t* y) {
   const bool bf16 = d->weight_format == MOE_W_BF16;  // no scale tensors
   if (!logits || !x || (!x_sf && !bf16) || !w1 || (!w1_sf && !bf16) || !w2 || (!w2_sf && !bf16) || !y)
     return fail(MOE_ERR_NULL, "a required pointer is NULL");
   if (misaligned(logits, 16) || misaligned(x, 16) || misaligned(x_sf, 16) || misaligned(w1, 16) ||
       misaligned(w1_sf, 16) || misaligned(w2, 16) || misaligned(w2_sf, 16) || misaligned(y, 16))
     return fail(MOE_ERR_MISALIGNED, "an input/output pointer is not 16-byte aligned");
-  if (moe_status st = check_ws(d, ws, ws_bytes)) return st;
-  if (moe_status st = check_device()) return st;
+  return MOE_OK;
+}
+
+// The whole layer on a validated descriptor, arguments and workspace.
+moe_status run_layer(const moe_layer_desc* d, const float* logits, const uint8_t* x, const uint8_t* x_sf,
+                     const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf, uint16_t* y,
+                     int32_t* opt_ids, float* opt_w, int32_t* opt_counts, int32_t* opt_offsets, int32_t* opt_r2s,
+                     int32_t* opt_s2r, void* ws, hipStream_t s) {
   const Layout L = make_layout(*d);
   const moe::Shape sh = shape_of(*d);
-  hipStream_t s = (hipStream_t)stream;
   int32_t* ids = opt_ids ? opt_ids : region<int32_t>(ws, L.ids);
   float* w = opt_w ? opt_w : region<float>(ws, L.w);
   int32_t* counts = opt_counts ? opt_counts : region<int32_t>(ws, L.counts);
@@ -339,6 +345,74 @@ moe_status moe_layer(const moe_layer_desc* d, const float* logits, const uint8_t
   MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, offsets + d->num_local,
                                   d->num_shared, y, s));
   return ok();
+}
+
+}  // namespace
+
+// Scratch of the no-allocation entry point: one array per device, held by the loaded code
+// object until the process ends.  In host code `scratch` names a host-side stand-in, not
+// the device array; the device address is looked up once per device (with that device
+// current) and only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];  // device address of `scratch` per device index, nullptr until looked up
+
+moe_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer(const moe_layer_desc* d, const float* logits, const uint8_t* x, const uint8_t* x_sf,
+                     const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf, uint16_t* y,
+                     int32_t* opt_ids, float* opt_w, int32_t* opt_counts, int32_t* opt_offsets, int32_t* opt_r2s,
+                     int32_t* opt_s2r, void* ws, size_t ws_bytes, void* stream) {
+  if (moe_status st = check_desc(d)) return st;
+  if (d->num_tokens == 0) return ok();
+  if (moe_status st = check_layer_args(d, logits, x, x_sf, w1, w1_sf, w2, w2_sf, y)) return st;
+  if (moe_status st = check_ws(d, ws, ws_bytes)) return st;
+  if (moe_status st = check_device()) return st;
+  return run_layer(d, logits, x, x_sf, w1, w1_sf, w2, w2_sf, y, opt_ids, opt_w, opt_counts, opt_offsets, opt_r2s,
+                   opt_s2r, ws, (hipStream_t)stream);
+}
+
+size_t moe_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+moe_status moe_layer_static(const moe_layer_desc* d, const float* logits, const uint8_t* x, const uint8_t* x_sf,
+                            const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf,
+                            uint16_t* y, int32_t* opt_ids, float* opt_w, int32_t* opt_counts, int32_t* opt_offsets,
+                            int32_t* opt_r2s, int32_t* opt_s2r, void* stream) {
+  if (moe_status st = check_desc(d)) return st;
+  if (d->num_tokens == 0) return ok();
+  if (moe_status st = check_layer_args(d, logits, x, x_sf, w1, w1_sf, w2, w2_sf, y)) return st;
+  const size_t need = make_layout(*d).total;
+  if (need > kStaticScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "layer needs %zu bytes of scratch, more than the static array's %zu; use moe_layer "
+                "with a caller-owned workspace", need, kStaticScratchBytes);
+  if (moe_status st = check_device()) return st;
+  void* ws = nullptr;
+  if (moe_status st = static_scratch(&ws)) return st;
+  return run_layer(d, logits, x, x_sf, w1, w1_sf, w2, w2_sf, y, opt_ids, opt_w, opt_counts, opt_offsets, opt_r2s,
+                   opt_s2r, ws, (hipStream_t)stream);
 }
 
 moe_status moe_quantize_act(const moe_layer_desc* d, const uint16_t* x_bf16, uint8_t* x, uint8_t* x_sf,

@@ -191,3 +191,15 @@ def test_probe_arguments_rejected_before_launch():
     assert lib.moe_probe_mfma_gemm(0, 1, 128, 0, None, fake, fake, None) == -1   # NULL operand
     assert lib.moe_probe_mfma_loop(0, 10, 0, fake, None) == -1
     assert lib.moe_probe_hbm_read(fake, 17, 1, fake, None) == -1                 # not whole 16-byte loads
+
+
+def test_static_scratch_entry_rejects_large_layers_before_launch(L):
+    """moe_layer_static refuses a layer whose scratch exceeds the static array, on the host,
+    before any device call (fake, never dereferenced pointers)."""
+    d = B.desc_from_workload(synth.workload("prefill_zipf"))
+    assert B.moe_workspace_size(d) > L.moe_static_scratch_bytes() == 64 * 2 ** 20
+    fake = ctypes.c_void_p(4096)
+    st = L.moe_layer_static(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, None, None, None, None,
+                            None, None, None)
+    assert st == B.MOE_ERR_WORKSPACE
+    assert b"static" in L.moe_last_error()
