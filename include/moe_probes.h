@@ -63,6 +63,14 @@ int moe_probe_mfma_loop(int blocks, int iters, int b_fp4, float* sink, void* str
  * float per thread to sink [blocks * 256].  1 <= blocks <= 2^20. */
 int moe_probe_hbm_read(const void* src, size_t bytes, int blocks, float* sink, void* stream);
 
+/* Scaled conversion probe: out[i] = the BF16 bits the gfx950 scaled conversion instruction
+ * gives for code i with scale 2^(scale_bytes[i/32] - 127), passed as the float whose bit
+ * pattern is scale_byte << 23 (the denormal 2^-127 for byte 0).  fmt 0: codes are E4M3 bytes
+ * [n]; 1: E5M2 bytes [n]; 2: E2M1 pairs [n/2], element 2i in the low nibble of byte i.
+ * scale_bytes [n/32]; out uint16 [n]; n a positive multiple of 32, at most 2^28. */
+int moe_probe_cvt_bf16(int fmt, int n, const uint8_t* codes, const uint8_t* scale_bytes, uint16_t* out,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,39 @@ __device__ __forceinline__ bf16x8 bf16_half(const v8i& v, int q) {
   return __builtin_bit_cast(bf16x8, h);
 }
 
+// UE8M0 byte -> the float 2^(byte - 127) handed to the scaled conversions (2^-127 is the
+// denormal 0x00400000)
+__device__ __forceinline__ float scale_f32(int byte) {
+  const uint32_t b = (uint32_t)byte & 0xffu;
+  return __uint_as_float(b == 0 ? 0x00400000u : b << 23);
+}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 join4(bf16x2 p0, bf16x2 p1, bf16x2 p2, bf16x2 p3) {
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+// group q (8 values, dwords 2q and 2q + 1) of a 32-byte FP8 fragment as BF16 values times sc;
+// E4M3 and E5M2 values have at most 3 significant bits, so every conversion is exact
+template <bool E5M2>
+__device__ __forceinline__ bf16x8 fp8_group_bf16(const v8i& v, int q, float sc) {
+  const uint32_t d0 = (uint32_t)v[2 * q], d1 = (uint32_t)v[2 * q + 1];
+  if constexpr (E5M2)
+    return join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, sc, false),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, sc, true),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, sc, false),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, sc, true));
+  else
+    return join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, false),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, true),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, false),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, true));
+}
+// group q (8 values, dword q) of a 16-byte E2M1 fragment as BF16 values times sc
+__device__ __forceinline__ bf16x8 fp4_group_bf16(const v8i& v, int q, float sc) {
+  const uint32_t d = (uint32_t)v[q];
+  return join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0), __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1),
+               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2), __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3));
+}
+
 constexpr int kGroupN = 8;     // n-tiles per group in the tile order
 constexpr int kMaxKSteps = 64; // K <= 8192 (scales of a tile are staged in LDS, one per 128-wide step)
 
@@ -84,6 +117,7 @@ struct GemmArgs {
   int k;                 // top-k (FC1 row -> token)
   int EL;                // routed local experts; shared experts EL .. EL + S - 1 follow them
   int S;                 // shared experts: each has the T rows [offsets[EL] + s T, + T), one per token
+  int routed;            // 1: the routed experts' rows are tiled too; 0: this launch tiles the shared experts only
   int T;
   int n_tiles;
   int act;
@@ -198,10 +232,19 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ plan, int
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
 constexpr int kWgPerCu = NSTAGE * Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>::STAGE <= 80 * 1024 ? 2 : 1;
 
-template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
+// XA (FC1 on FP8 / MXFP4 data only): exact-sum FC1.  The scaled FP8 MFMA's sums carry an error
+// near 1.5e-5 of their value (measured: the same for every FP8 instruction form, so it comes from
+// how the hardware adds the FP8 products, not from chaining), which flips requantised h codes that
+// lie that close to an E4M3 rounding midpoint.  XA converts each operand fragment to BF16 in
+// registers with its UE8M0 block scale folded in (exact: the codes have at most 3 significant
+// bits) and multiplies with the BF16 MFMA, whose fp32 sums match a sequential fp32 sum of the
+// exact products.  It costs conversion instructions and half the matrix-core rate, which is
+// free where the GEMM streams weights (few rows per expert).
+template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE, int XA>
 __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>)) void grouped_gemm_kernel(
     GemmArgs g) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
+  static_assert(!XA || (MODE == 1 && WFMT != 3), "exact-sum FC1 is for the scaled formats");
   using F = Frags<C::MI, C::NT, C::NH>;
   // LDS (dynamic, sized at launch): the stage ring, then the tile's activation scales
   // [row][ks128] and FP8 weight scales [block][ks128].  The token list of the tile rows and
@@ -237,7 +280,7 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     for (int j = 0; j < per; ++j) {
       const int ee = beg + j;
       if (ee < n) s_plan[ee] = sum;
-      if (ee < g.EL) sum += (g.offsets[ee + 1] - g.offsets[ee] + BM - 1) / BM;
+      if (ee < g.EL) sum += g.routed ? (g.offsets[ee + 1] - g.offsets[ee] + BM - 1) / BM : 0;
       else if (ee < n - 1) sum += (g.T + BM - 1) / BM;
     }
     const int inc = wave_inclusive_scan(sum);
@@ -414,7 +457,11 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   uint32_t a_lds[2], b_lds[2];
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi) {
-    a_lds[hi] = ra * C::A_ROWB + (((2 * hi + kb) ^ swz<C::A_CPR>(ra)) << 4);
+    // exact-sum FC1 on MXFP4 weights reads a token fragment as the contiguous K values
+    // [32 kb, +32) of the 64-wide step (chunks 2 kb and 2 kb + 1), the K values of the
+    // weight fragment it is multiplied with
+    const int achunk = (XA && WFMT == 1) ? 2 * kb + hi : 2 * hi + kb;
+    a_lds[hi] = ra * C::A_ROWB + ((achunk ^ swz<C::A_CPR>(ra)) << 4);
     b_lds[hi] = WFMT != 1 ? rb * C::B_ROWB + (((2 * hi + kb) ^ swz<C::B_CPR>(rb)) << 4)
                            : rb * C::B_ROWB + ((kb ^ swz<C::B_CPR>(rb)) << 4);
   }
@@ -472,6 +519,33 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   auto mma_n = [&](const auto& f, auto nl) {
     constexpr int NL = decltype(nl)::value;
     constexpr int NHF = sizeof(f.b) / sizeof(f.b[0]);
+    if constexpr (XA) {
+      // four BF16 MFMAs per 64-wide K step: group q of the lane's values of both operands (the
+      // same K positions in both), scales folded into the conversions
+#pragma unroll
+      for (int h = 0; h < NHF; ++h) {
+        bf16x8 tq[NL][4];
+#pragma unroll
+        for (int mi = 0; mi < NL; ++mi) {
+          const float sc = scale_f32(f.sa[mi]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) tq[mi][q] = fp8_group_bf16<false>(f.a[h][mi], q, sc);
+        }
+#pragma unroll
+        for (int ct = 0; ct < C::NT; ++ct) {
+          const float sc = scale_f32(f.sb[h][ct]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x8 wq = WFMT == 1 ? fp4_group_bf16(f.b[h][ct], q, sc)
+                                        : fp8_group_bf16<WFMT == 2>(f.b[h][ct], q, sc);
+#pragma unroll
+            for (int mi = 0; mi < NL; ++mi)
+              acc[mi][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wq, tq[mi][q], acc[mi][ct], 0, 0, 0);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < NHF; ++h)
 #pragma unroll
@@ -763,13 +837,13 @@ size_t gemm_max_mtiles(int rows_cap, int EL, int variant, int T, int S) {
 
 bool gemm_supports(int H, int I) { return H / 128 <= kMaxKSteps && I / 128 <= kMaxKSteps; }
 
-template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
+template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE, int XA>
 static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   static_assert(NSTAGE * C::STAGE >= BM * 128 + C::WN * BM * 4 + BM && NSTAGE * C::STAGE >= BM * 4 + BM * 128 &&
                     (!C::BF16 || NSTAGE * C::STAGE >= BM * 256),
                 "the ring must hold the epilogue staging and the tile's token list");
-  auto kern = grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
+  auto kern = grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE, XA>;
   const size_t lds = (size_t)NSTAGE * C::STAGE + (size_t)BM * (a.K / 128) + 2 * (a.K / 128);
   // raise the kernel's dynamic LDS limit to its largest size (K = 8192) once per device
   static std::atomic<uint64_t> ready{0};
@@ -787,37 +861,44 @@ static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int MODE, int WFMT>
+template <int MODE, int WFMT, int XA>
 static hipError_t launch_variant_w(const GemmArgs& a, int variant, size_t grid, hipStream_t s) {
   // 256-row tiles: eight waves of 64 x 128; MXFP4 FC1 (half the weight bytes per stage, so
   // the MFMAs and LDS reads decide) runs faster as four waves of 128 x 128, accumulators in
   // AGPRs (measured on the 32768-token share: 0.941 against 0.977 ms)
   if (variant == 1) {
-    if constexpr (MODE == 1 && WFMT == 1) return launch_one<MODE, WFMT, 256, 256, 128, 2, 4, 128, 2>(a, grid, s);
-    else return launch_one<MODE, WFMT, 256, 256, 128, 2, 8, 64, 2>(a, grid, s);
+    if constexpr (MODE == 1 && WFMT == 1) return launch_one<MODE, WFMT, 256, 256, 128, 2, 4, 128, 2, XA>(a, grid, s);
+    else return launch_one<MODE, WFMT, 256, 256, 128, 2, 8, 64, 2, XA>(a, grid, s);
   }
   if (variant == 2) {
-    if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 32, 256, 128, 3, 4, 32, 2>(a, grid, s);
-    else return launch_one<MODE, WFMT, 32, 256, 128, 2, 4, 32, 2>(a, grid, s);
+    if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 32, 256, 128, 3, 4, 32, 2, XA>(a, grid, s);
+    else return launch_one<MODE, WFMT, 32, 256, 128, 2, 4, 32, 2, XA>(a, grid, s);
   }
   // experts with tens of rows: FC2 tiles are 128 columns wide, two workgroups of 8 waves
   // per CU (one streams weights while the other is in its prologue or epilogue); FC1 streams
   // whole 128-byte weight-row segments through a three-stage ring, one workgroup of 8 waves
   // per CU (two per SIMD, so one wave's LDS reads overlap the other's MFMAs), except MXFP4,
   // whose 64-byte stages keep two workgroups per CU
-  if constexpr (MODE == 2) return launch_one<MODE, WFMT, 128, 128, 128, 2, 8, 32, 0>(a, grid, s);
-  else if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 128, 256, 64, 4, 4, 64, 0>(a, grid, s);
-  else return launch_one<MODE, WFMT, 128, 256, 128, 3, 8, 32, 0>(a, grid, s);
+  if constexpr (MODE == 2) return launch_one<MODE, WFMT, 128, 128, 128, 2, 8, 32, 0, XA>(a, grid, s);
+  else if constexpr (WFMT == 1) return launch_one<MODE, WFMT, 128, 256, 64, 4, 4, 64, 0, XA>(a, grid, s);
+  else return launch_one<MODE, WFMT, 128, 256, 128, 3, 8, 32, 0, XA>(a, grid, s);
 }
 
 // weight formats: 0 FP8 E4M3 with 128x128 scales, 1 MXFP4, 2 FP8 E5M2 with 128x128 scales,
 // 3 BF16 (activations, weights and the intermediate all BF16, no scales)
 template <int MODE>
-static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, size_t grid, hipStream_t s) {
-  if (wfmt == 1) return launch_variant_w<MODE, 1>(a, variant, grid, s);
-  if (wfmt == 2) return launch_variant_w<MODE, 2>(a, variant, grid, s);
-  if (wfmt == 3) return launch_variant_w<MODE, 3>(a, variant, grid, s);
-  return launch_variant_w<MODE, 0>(a, variant, grid, s);
+static hipError_t launch_variant(const GemmArgs& a, int wfmt, int variant, bool exact, size_t grid, hipStream_t s) {
+  if constexpr (MODE == 1) {
+    if (exact && wfmt != 3) {
+      if (wfmt == 1) return launch_variant_w<MODE, 1, 1>(a, variant, grid, s);
+      if (wfmt == 2) return launch_variant_w<MODE, 2, 1>(a, variant, grid, s);
+      return launch_variant_w<MODE, 0, 1>(a, variant, grid, s);
+    }
+  }
+  if (wfmt == 1) return launch_variant_w<MODE, 1, 0>(a, variant, grid, s);
+  if (wfmt == 2) return launch_variant_w<MODE, 2, 0>(a, variant, grid, s);
+  if (wfmt == 3) return launch_variant_w<MODE, 3, 0>(a, variant, grid, s);
+  return launch_variant_w<MODE, 0, 0>(a, variant, grid, s);
 }
 
 // per-tensor scaling: the scale tensors hold float32 values (x: one, weights: one per expert)
@@ -830,42 +911,75 @@ static void set_tensor_scales(GemmArgs& a, const Shape& sh, const float* a_scale
   a.h_inv = 1.0f / sh.h_scale;
 }
 
-hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
-                      const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
-                      uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s) {
+// Shared experts have exactly T rows each, known on the host, so they may use another tile shape
+// than the routed experts (variant_shared); then the routed and the shared experts' tiles are two
+// launches of the same kernel family, the second with its tile plan over the shared experts only.
+hipError_t launch_fc1(const Shape& sh, int variant, int variant_shared, const uint8_t* x, const uint8_t* x_sf,
+                      const uint8_t* w1, const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot,
+                      uint8_t* h, uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s) {
   GemmArgs a{};
   a.A = x; a.A_sf = x_sf; a.row_to_slot = row_to_slot; a.B = w1; a.B_sf = w1_sf;
-  // the permute's tile plan covers the routed experts only
-  a.offsets = offsets; a.plan = plan_ready && sh.S == 0 ? plan : nullptr; a.h = h; a.h_sf = h_sf;
-  a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.S = sh.S; a.T = sh.T; a.n_tiles = sh.I / 128;
+  a.offsets = offsets; a.h = h; a.h_sf = h_sf;
+  a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.T = sh.T; a.n_tiles = sh.I / 128;
   a.b_estride = sh.wfmt == 3 ? (long long)2 * sh.I * sh.H * 2
                 : sh.wfmt != 1 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
   a.act = sh.act; a.clamp = sh.clamp; a.alpha = sh.alpha; a.bias = sh.bias;
   set_tensor_scales(a, sh, reinterpret_cast<const float*>(x_sf), reinterpret_cast<const float*>(w1_sf));
-  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, sh.S) * (size_t)a.n_tiles;
-  if (grid == 0) return hipSuccess;
+  const bool split = sh.S > 0 && variant_shared != variant;
+  // routed experts (and the shared ones unless they take their own launch); the permute's tile
+  // plan covers the routed experts only
+  a.routed = 1;
+  a.S = split ? 0 : sh.S;
+  a.plan = plan_ready && a.S == 0 ? plan : nullptr;
+  size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, a.S) * (size_t)a.n_tiles;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  return launch_variant<1>(a, sh.wfmt, variant, grid, s);
+  if (grid > 0) {
+    const hipError_t e = launch_variant<1>(a, sh.wfmt, variant, sh.exact_fc1, grid, s);
+    if (e != hipSuccess || !split) return e;
+  } else if (!split) {
+    return hipSuccess;
+  }
+  a.routed = 0;
+  a.S = sh.S;
+  a.plan = nullptr;
+  const int bm = gemm_block_m(variant_shared);
+  grid = (size_t)sh.S * (((size_t)sh.T + bm - 1) / bm) * (size_t)a.n_tiles;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  return launch_variant<1>(a, sh.wfmt, variant_shared, sh.exact_fc1, grid, s);
 }
 
-hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
-                      const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, bool plan_ready,
-                      hipStream_t s) {
+hipError_t launch_fc2(const Shape& sh, int variant, int variant_shared, const uint8_t* h, const uint8_t* h_sf,
+                      const uint8_t* w2, const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan,
+                      bool plan_ready, hipStream_t s) {
   GemmArgs a{};
   a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets;
-  a.plan = plan_ready && sh.S == 0 ? plan : nullptr;
   a.y2 = y2;
-  a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.S = sh.S; a.T = sh.T;
+  a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.T = sh.T;
   a.b_estride = sh.wfmt == 3 ? (long long)sh.H * sh.I * 2 : sh.wfmt != 1 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
   set_tensor_scales(a, sh, nullptr, reinterpret_cast<const float*>(w2_sf));
-  const int bn = variant == 0 ? 128 : 256;
-  a.n_tiles = (sh.H + bn - 1) / bn;
-  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, sh.S) * (size_t)a.n_tiles;
-  if (grid == 0) return hipSuccess;
+  const bool split = sh.S > 0 && variant_shared != variant;
+  a.routed = 1;
+  a.S = split ? 0 : sh.S;
+  a.plan = plan_ready && a.S == 0 ? plan : nullptr;
+  a.n_tiles = (sh.H + (variant == 0 ? 128 : 256) - 1) / (variant == 0 ? 128 : 256);
+  size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, a.S) * (size_t)a.n_tiles;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  return launch_variant<2>(a, sh.wfmt, variant, grid, s);
+  if (grid > 0) {
+    const hipError_t e = launch_variant<2>(a, sh.wfmt, variant, false, grid, s);
+    if (e != hipSuccess || !split) return e;
+  } else if (!split) {
+    return hipSuccess;
+  }
+  a.routed = 0;
+  a.S = sh.S;
+  a.plan = nullptr;
+  a.n_tiles = (sh.H + (variant_shared == 0 ? 128 : 256) - 1) / (variant_shared == 0 ? 128 : 256);
+  const int bm = gemm_block_m(variant_shared);
+  grid = (size_t)sh.S * (((size_t)sh.T + bm - 1) / bm) * (size_t)a.n_tiles;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  return launch_variant<2>(a, sh.wfmt, variant_shared, false, grid, s);
 }
 
 }  // namespace moe

@@ -157,11 +157,27 @@ moe_status check_device() {
   return MOE_OK;
 }
 
+// Whether FC1 sums exactly: BF16 MFMAs on operands converted in registers instead of the scaled
+// FP8 MFMA (see the GEMM source).  That costs conversion instructions and half the matrix-core
+// rate, which is free where the GEMM streams weights: at most 48 rows per local expert on
+// average (the 32-row tile regime, fewer than ~100 FLOPs per weight byte), or a layer whose FC1
+// is at most 2^33 FLOPs (a few microseconds of work, launch- and latency-bound).  Larger layers
+// keep the scaled FP8 MFMA (measured on the 512-token, 2048-hidden OAI share: the exact FC1 took
+// 37.9 instead of 25.3 us).
+bool exact_fc1(const moe_layer_desc& d) {
+  if (d.weight_format == MOE_W_BF16) return false;
+  const long long rows = (long long)d.num_tokens * (d.topk < d.num_local ? d.topk : d.num_local);
+  const long long all_rows = rows + (long long)d.num_shared * d.num_tokens;
+  const double fc1_flops = 4.0 * (double)all_rows * d.hidden * d.inter;
+  return rows <= 48LL * d.num_local || fc1_flops <= 8589934592.0;
+}
+
 moe::Shape shape_of(const moe_layer_desc& d) {
   moe::Shape s;
   s.T = d.num_tokens; s.H = d.hidden; s.I = d.inter; s.E = d.num_experts; s.e0 = d.local_begin;
   s.EL = d.num_local; s.k = d.topk; s.wfmt = d.weight_format; s.act = d.activation;
   s.S = d.num_shared;
+  s.exact_fc1 = exact_fc1(d);
   s.tensor = d.scale_mode == MOE_SCALE_TENSOR;
   s.h_scale = s.tensor ? d.h_scale : 1.f;
   if (d.activation == MOE_ACT_SWIGLU_OAI) {
@@ -182,6 +198,15 @@ int pick_variant(const moe_layer_desc& d) {
   const long long most_rows = (long long)d.num_tokens * (d.topk < d.num_local ? d.topk : d.num_local);
   if (most_rows >= 256LL * d.num_local) return 1;
   if (most_rows <= 48LL * d.num_local) return 2;
+  return 0;
+}
+
+// Tile variant of the shared experts: each has exactly T rows, which the host knows, so the
+// same thresholds as above apply to T itself (a forced variant applies to every expert).
+int pick_shared_variant(const moe_layer_desc& d) {
+  if (d.variant >= 0) return d.variant;
+  if (d.num_tokens >= 256) return 1;
+  if (d.num_tokens <= 48) return 2;
   return 0;
 }
 
@@ -276,7 +301,7 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* d, const uint8_t* x, con
   if (moe_status st = check_ws(d, ws, ws_bytes)) return st;
   if (moe_status st = check_device()) return st;
   const moe::Shape sh = shape_of(*d);
-  MOE_TRY_HIP(moe::launch_fc1(sh, pick_variant(*d), x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
+  MOE_TRY_HIP(moe::launch_fc1(sh, pick_variant(*d), pick_shared_variant(*d), x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
                               nullptr, false, (hipStream_t)stream));
   return ok();
 }
@@ -297,7 +322,7 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* d, const uint8_t* h, co
   const Layout L = make_layout(*d);
   const moe::Shape sh = shape_of(*d);
   float* y2 = region<float>(ws, L.y2);
-  MOE_TRY_HIP(moe::launch_fc2(sh, pick_variant(*d), h, h_sf, w2, w2_sf, offsets, y2, nullptr,
+  MOE_TRY_HIP(moe::launch_fc2(sh, pick_variant(*d), pick_shared_variant(*d), h, h_sf, w2, w2_sf, offsets, y2, nullptr,
                               false, (hipStream_t)stream));
   MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, offsets + d->num_local,
                                   d->num_shared, y, (hipStream_t)stream));
@@ -339,9 +364,11 @@ moe_status run_layer(const moe_layer_desc* d, const float* logits, const uint8_t
   const int variant = pick_variant(*d);
   if (moe_status st = run_route_permute(*d, L, logits, ids, w, counts, offsets, r2s, s2r, ws, s)) return st;
   // the permute wrote the tile plan of these offsets (plan1) for this variant's tile rows
-  MOE_TRY_HIP(moe::launch_fc1(sh, variant, x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf, region<int32_t>(ws, L.plan1),
-                              true, s));
-  MOE_TRY_HIP(moe::launch_fc2(sh, variant, h, h_sf, w2, w2_sf, offsets, y2, region<int32_t>(ws, L.plan1), true, s));
+  const int variant_shared = pick_shared_variant(*d);
+  MOE_TRY_HIP(moe::launch_fc1(sh, variant, variant_shared, x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
+                              region<int32_t>(ws, L.plan1), true, s));
+  MOE_TRY_HIP(moe::launch_fc2(sh, variant, variant_shared, h, h_sf, w2, w2_sf, offsets, y2,
+                              region<int32_t>(ws, L.plan1), true, s));
   MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, offsets + d->num_local,
                                   d->num_shared, y, s));
   return ok();

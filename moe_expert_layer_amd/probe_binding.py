@@ -30,6 +30,8 @@ def lib():
         L.moe_probe_mfma_loop.argtypes = [I32, I32, I32, P, P]
         L.moe_probe_hbm_read.restype = I32
         L.moe_probe_hbm_read.argtypes = [P, ctypes.c_size_t, I32, P, P]
+        L.moe_probe_cvt_bf16.restype = I32
+        L.moe_probe_cvt_bf16.argtypes = [I32, I32, P, P, P, P]
         _lib = L
     return _lib
 
@@ -59,3 +61,9 @@ def mfma_loop(blocks: int, iters: int, sink, b_fp4: bool = False, stream=None):
 def hbm_read(src, blocks: int, sink, stream=None):
     _check(lib().moe_probe_hbm_read(src.data_ptr(), src.numel() * src.element_size(), blocks, sink.data_ptr(),
                                     _stream(stream)), "moe_probe_hbm_read")
+
+
+def cvt_bf16(fmt: int, codes, scale_bytes, out, stream=None):
+    """fmt 0 E4M3, 1 E5M2, 2 E2M1 pairs; out uint16/int16 [n] (n = values)."""
+    _check(lib().moe_probe_cvt_bf16(fmt, out.numel(), codes.data_ptr(), scale_bytes.data_ptr(), out.data_ptr(),
+                                    _stream(stream)), "moe_probe_cvt_bf16")

@@ -155,25 +155,20 @@ __global__ __launch_bounds__(64) void probe_gemm_kernel(int form, int K, const u
 
 // Four independent accumulators per wave, operands in registers: the instruction issue rate
 // is the only limit.  The operand bytes are finite FP8 / FP4 values that differ per lane.
-__global__ __launch_bounds__(256) void probe_mfma_loop_kernel(int iters, int b_fp4, float* __restrict__ sink) {
+template <int BF4>
+__global__ __launch_bounds__(256) void probe_mfma_loop_kernel(int iters, float* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
   const int pat = 0x38383838 ^ ((lane & 7) * 0x01010101);  // E4M3 values near 1
   const v8i av = v8i{pat, pat, pat, pat, pat, pat, pat, pat};
   const int fp4pat = 0x22222222 ^ ((lane & 3) * 0x11111111);
-  const v8i bv = b_fp4 ? v8i{fp4pat, fp4pat, fp4pat, fp4pat, 0, 0, 0, 0} : av;
+  const v8i bv = BF4 ? v8i{fp4pat, fp4pat, fp4pat, fp4pat, 0, 0, 0, 0} : av;
+  constexpr int bcode = BF4 ? 4 : 0;
   v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
   for (int it = 0; it < iters; ++it) {
-    if (b_fp4) {
-      c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c0, 0, 4, 0, 120, 0, 120);
-      c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c1, 0, 4, 0, 120, 0, 120);
-      c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c2, 0, 4, 0, 120, 0, 120);
-      c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c3, 0, 4, 0, 120, 0, 120);
-    } else {
-      c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c0, 0, 0, 0, 120, 0, 120);
-      c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c1, 0, 0, 0, 120, 0, 120);
-      c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c2, 0, 0, 0, 120, 0, 120);
-      c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c3, 0, 0, 0, 120, 0, 120);
-    }
+    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c0, 0, bcode, 0, 120, 0, 120);
+    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c1, 0, bcode, 0, 120, 0, 120);
+    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c2, 0, bcode, 0, 120, 0, 120);
+    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c3, 0, bcode, 0, 120, 0, 120);
   }
   float s = 0.f;
 #pragma unroll
@@ -203,9 +198,36 @@ __global__ __launch_bounds__(256) void probe_hbm_read_kernel(const v4i_* __restr
   sink[(long long)blockIdx.x * 256 + threadIdx.x] = (float)(acc & 0xffff);
 }
 
+// value i of the output: code i (E4M3, E5M2 or E2M1) converted to BF16 with the scale
+// 2^(scale_bytes[i / 32] - 127) passed to the conversion instruction as the float whose bits are
+// scale_byte << 23 (2^-127 as the denormal 0x00400000 for byte 0)
+__global__ __launch_bounds__(256) void probe_cvt_kernel(int fmt, int n, const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ sbytes, uint16_t* __restrict__ out) {
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 2;  // two values per thread
+  if (i >= n) return;
+  const uint32_t sb = sbytes[i / 32];
+  const float sc = __uint_as_float(sb == 0 ? 0x00400000u : sb << 23);
+  bf16x2 r;
+  if (fmt == 2) {  // E2M1: values i, i+1 are the two nibbles of byte i/2
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)codes[i / 2], sc, 0);
+  } else {
+    const uint32_t v = (uint32_t)codes[i] | ((uint32_t)codes[i + 1] << 8);
+    r = fmt == 1 ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(v, sc, false)
+                 : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, sc, false);
+  }
+  *reinterpret_cast<uint32_t*>(out + i) = __builtin_bit_cast(uint32_t, r);  // i even: value i in the low half
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_probe_cvt_bf16(int fmt, int n, const uint8_t* codes, const uint8_t* scale_bytes, uint16_t* out, void* stream) {
+  if (fmt < 0 || fmt > 2 || n < 2 || n % 32 || n > (1 << 28) || !codes || !scale_bytes || !out) return -1;
+  probe_cvt_kernel<<<dim3((n / 2 + 255) / 256), 256, 0, (hipStream_t)stream>>>(fmt, n, codes, scale_bytes, out);
+  return (int)hipGetLastError();
+}
+
 
 int moe_probe_mfma_gemm(int form, int n, int K, int b_fp4, const uint8_t* a, const uint8_t* b, float* c,
                         void* stream) {
@@ -218,7 +240,8 @@ int moe_probe_mfma_gemm(int form, int n, int K, int b_fp4, const uint8_t* a, con
 
 int moe_probe_mfma_loop(int blocks, int iters, int b_fp4, float* sink, void* stream) {
   if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20) || !sink) return -1;
-  probe_mfma_loop_kernel<<<dim3(blocks), 256, 0, (hipStream_t)stream>>>(iters, b_fp4 ? 1 : 0, sink);
+  if (b_fp4) probe_mfma_loop_kernel<1><<<dim3(blocks), 256, 0, (hipStream_t)stream>>>(iters, sink);
+  else probe_mfma_loop_kernel<0><<<dim3(blocks), 256, 0, (hipStream_t)stream>>>(iters, sink);
   return (int)hipGetLastError();
 }
 

@@ -104,3 +104,40 @@ def test_mfma_accumulation_precision(fp4):
     assert res["fp32_fma"]["rel_fro"] < 1e-6
     for form, r in res.items():
         assert r["rel_fro"] < 1e-3, (form, r)
+
+
+def _bf16_bits_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2], ids=["e4m3", "e5m2", "e2m1"])
+def test_scaled_conversion_to_bf16_is_exact(fmt):
+    """The scaled conversions (FP8 / FP4 code x 2^(byte - 127) -> BF16) that an exact-sum FC1 can use
+    to fold the UE8M0 block scales into its operands: every code under a spread of scale bytes
+    gives exactly code * 2^(byte - 127) wherever that value is a normal BF16 number (all E4M3,
+    E5M2 and E2M1 values have at most 3 significant bits, so the product is representable)."""
+    scales = np.array([1, 40, 100, 120, 127, 128, 135, 160, 200, 240], np.uint8)
+    if fmt == 2:
+        codes = np.tile(np.arange(256, dtype=np.uint8), 2 * len(scales))  # every pair of nibbles
+        n = codes.size * 2
+        lo, hi = _E2M1[codes & 15], _E2M1[codes >> 4]
+        v = np.empty(n)
+        v[0::2], v[1::2] = lo, hi
+    else:
+        vals = np.array([c for c in range(256) if not ((fmt == 0 and (c & 0x7F) == 0x7F) or (fmt == 1 and (c & 0x7C) == 0x7C))],
+                        np.uint8)
+        codes = np.resize(vals, 32 * len(scales) * 8)
+        n = codes.size
+        tt = torch.float8_e4m3fn if fmt == 0 else torch.float8_e5m2
+        v = torch.from_numpy(codes.copy()).view(tt).to(torch.float64).numpy()
+    sb = np.resize(scales, n // 32).astype(np.uint8)
+    expect = v * np.ldexp(1.0, sb.repeat(32).astype(np.int64) - 127)
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    P.cvt_bf16(fmt, torch.from_numpy(codes).cuda(), torch.from_numpy(sb).cuda(), out)
+    torch.cuda.synchronize()
+    got = _bf16_bits_to_f64(out.cpu().numpy().view(np.uint16))
+    normal = (np.abs(expect) >= 2.0 ** -126) & (np.abs(expect) < 2.0 ** 127) | (expect == 0)
+    bad = normal & (got != expect)
+    G.say(f"[cvt] fmt={fmt}: {int(normal.sum())} in-range values, {int(bad.sum())} differ")
+    assert not bad.any(), list(zip(codes[np.nonzero(bad)[0][:4] // (2 if fmt == 2 else 1)], got[bad][:4], expect[bad][:4]))
+    assert normal.mean() > 0.75

@@ -9,9 +9,8 @@ Checks, for the three-call path and the one-call entry point:
 * every token whose intermediate rows all equal the oracle's bit for bit: y within one
   bfloat16 step plus 1e-4 of the token's largest |y| (FC2 runs on identical inputs there,
   so only the MFMA's own rounding and the final bf16 rounding remain);
-* with 256 or more rows, the relative Frobenius error of y within the 2e-3 bar (below that,
-  a single requantisation flip, itself within one grid step, can move a tiny layer's norm
-  by more than the bar).
+* the relative Frobenius error of y within the 2e-3 bar, for every draw (layers of this size
+  sum FC1 exactly, so requantised h codes flip only where fp32 rounding itself decides).
 """
 import os
 
@@ -81,8 +80,7 @@ def _check(name, w, got, ref):
         assert not bad.any(), (name, t, np.nonzero(bad)[0][:8], a[t][bad][:4], b[t][bad][:4])
     err = G.rel_fro(a, b)
     G.say(f"[random] {name}: R={R} clean tokens {clean}/{T} rel_fro={err:.3e} h_bytes_equal={be:.5f}")
-    if R + S * T >= 256:
-        assert err <= TOL, (name, err)
+    assert err <= TOL, (name, err)
     return err
 
 
@@ -99,3 +97,20 @@ def test_random_config_against_oracle(i):
     _check(f"case {i}", w, got, ref)
     one = G.run_layer(w, dev, variant=variant)
     assert np.array_equal(one["y_bf16"], got["y_bf16"])
+
+
+@pytest.mark.parametrize("i", [171, 216])
+def test_named_sweep_draws(i):
+    """Two draws of the 300-draw sweep that once missed the 2e-3 bar (2.03e-3: MXFP4, T = 288,
+    H = 640, I = 256, a two-expert share every token reaches; 2.22e-3: FP8, T = 209, H = 512,
+    I = 128).  Their excess came from requantised h codes flipped by the FP8 matrix
+    instructions' summation error; layers of this size now sum FC1 exactly."""
+    w, variant = random_case(i)
+    G.say(f"[random] named draw {i}: T={w.tokens} H={w.hidden} I={w.inter} E={w.num_experts} EL={w.num_local} "
+          f"k={w.topk} fmt={w.weight_format} variant={variant}")
+    inp = synth.generate(w)
+    ref = O.layer(w, inp)
+    dev = G.upload(inp)
+    got = G.run_split(w, dev, variant=variant)
+    err = _check(f"draw {i}", w, got, ref)
+    assert err <= TOL, err
