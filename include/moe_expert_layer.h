@@ -26,7 +26,8 @@
  *     ignored (every counter the kernels use is initialised inside the call).
  *   - Layouts are row-major and dense:
  *       logits      float32 [T, E_tot]
- *       x           E4M3 bytes [T, H]            x_sf   UE8M0 bytes [T, H/128]
+ *       x           E4M3 bytes [T, H]            x_sf   UE8M0 bytes [T, H/128] (or packed, see
+ *                                                moe_sf_layout)
  *       w1 (fp8)    E4M3 or E5M2 bytes [E_loc, 2I, H]  w1_sf  UE8M0 [E_loc, 2I/128, H/128]
  *       w1 (mxfp4)  E2M1 pairs [E_loc, 2I, H/2]        w1_sf  UE8M0 [E_loc, 2I, H/32]
  *       w2 (fp8)    E4M3 or E5M2 bytes [E_loc, H, I]   w2_sf  UE8M0 [E_loc, H/128, I/128]
@@ -97,7 +98,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -114,6 +115,17 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 } moe_act;
 
 /* Scaling: blockwise UE8M0 (the default) or one float32 scale per tensor (see above). */
 typedef enum { MOE_SCALE_BLOCK = 0, MOE_SCALE_TENSOR = 1 } moe_scale;
+
+/* Layout of the 1x128 activation scale tensors x_sf and h_sf (blockwise scaling only):
+ * MOE_SF_ROW_MAJOR: UE8M0 bytes [rows, groups] (the default; groups = H/128 or I/128);
+ * MOE_SF_PACKED_MN: the packed int32 MN-major tensor of "DSV4 o_proj: fuse fp8/UE8M0 quantize
+ *   into o_a proj" (Description: shape (rows, ceil(groups/4)), stride (1, aligned_rows),
+ *   aligned_rows = rows rounded up to 4): word (m, j) at int32 index j * aligned_rows + m holds
+ *   groups 4j..4j+3 of row m, group 4j+b in byte b (the layout moe_pack_scales writes).  The
+ *   GEMMs read x_sf (rows = T) and FC1 writes / FC2 reads h_sf (rows = T*k + S*T) in this
+ *   layout directly; FC1 writes only the bytes of real groups and rows (padding is not
+ *   written and not read). */
+typedef enum { MOE_SF_ROW_MAJOR = 0, MOE_SF_PACKED_MN = 1 } moe_sf_layout;
 
 /* Weight formats: FP8 E4M3 or E5M2 with 128x128 UE8M0 block scales, or MXFP4 (E2M1, UE8M0
  * per 32 along K).  The FP8 weight formats are the ones the Hopper CuTeDSL MegaMoE kernel
@@ -143,6 +155,7 @@ typedef struct {
   int32_t scale_mode;     /* moe_scale; default MOE_SCALE_BLOCK */
   float h_scale;          /* MOE_SCALE_TENSOR only: static scale of the intermediate h */
   int32_t num_shared;     /* S in [0, 4]: shared experts applied to every token with weight 1 */
+  int32_t scale_layout;   /* moe_sf_layout of x_sf and h_sf; default MOE_SF_ROW_MAJOR */
 } moe_layer_desc;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION at build time). */

@@ -21,6 +21,8 @@ MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = 0, 1
 MOE_W_FP8_E4M3_B128, MOE_W_MXFP4_E2M1_B32, MOE_W_FP8_E5M2_B128, MOE_W_BF16 = 0, 1, 2, 3
 ACTIVATIONS = {"swiglu": MOE_ACT_SWIGLU, "swigluoai": MOE_ACT_SWIGLU_OAI}
 MOE_SCALE_BLOCK, MOE_SCALE_TENSOR = 0, 1
+MOE_SF_ROW_MAJOR, MOE_SF_PACKED_MN = 0, 1
+SCALE_LAYOUTS = {"rows": MOE_SF_ROW_MAJOR, "packed": MOE_SF_PACKED_MN}
 SCALINGS = {"block": MOE_SCALE_BLOCK, "tensor": MOE_SCALE_TENSOR}
 WEIGHT_FORMATS = {"fp8": MOE_W_FP8_E4M3_B128, "mxfp4": MOE_W_MXFP4_E2M1_B32, "fp8e5m2": MOE_W_FP8_E5M2_B128, "bf16": MOE_W_BF16}
 
@@ -32,7 +34,7 @@ class MoeLayerDesc(ctypes.Structure):
         ("topk", ctypes.c_int32), ("weight_format", ctypes.c_int32), ("activation", ctypes.c_int32),
         ("act_clamp", ctypes.c_float), ("act_alpha", ctypes.c_float), ("act_up_bias", ctypes.c_float),
         ("variant", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("h_scale", ctypes.c_float),
-        ("num_shared", ctypes.c_int32),
+        ("num_shared", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
     ]
 
 
@@ -97,12 +99,13 @@ def make_desc(num_tokens: int, hidden: int, inter: int, num_experts: int, topk: 
               num_local: Optional[int] = None, weight_format: str = "fp8", activation: str = "swiglu",
               activation_clamp: Optional[float] = None, activation_alpha: float = 1.0,
               activation_up_bias: float = 0.0, variant: int = -1, scaling: str = "block",
-              h_scale: float = 1.0, num_shared: int = 0) -> MoeLayerDesc:
+              h_scale: float = 1.0, num_shared: int = 0, scale_layout: str = "rows") -> MoeLayerDesc:
     """Descriptor with the pages' keyword names (activation, activation_clamp/alpha/up_bias).
 
     weight_format: "fp8" (E4M3), "fp8e5m2", "mxfp4" or "bf16" (the whole layer in BF16);
     scaling: "block" (UE8M0 scale tensors) or "tensor" (float32 scales, static h_scale);
-    num_shared: shared experts after the local ones in the weight tensors."""
+    num_shared: shared experts after the local ones in the weight tensors;
+    scale_layout: "rows" (UE8M0 bytes [rows, groups]) or "packed" (int32 MN-major words) for x_sf / h_sf."""
     d = MoeLayerDesc()
     _check(lib().moe_desc_defaults(ctypes.byref(d)))
     d.num_tokens, d.hidden, d.inter = num_tokens, hidden, inter
@@ -117,13 +120,15 @@ def make_desc(num_tokens: int, hidden: int, inter: int, num_experts: int, topk: 
     d.scale_mode = SCALINGS[scaling]
     d.h_scale = h_scale
     d.num_shared = num_shared
+    d.scale_layout = SCALE_LAYOUTS[scale_layout]
     return d
 
 
-def desc_from_workload(w, variant: int = -1) -> MoeLayerDesc:
+def desc_from_workload(w, variant: int = -1, scale_layout: str = "rows") -> MoeLayerDesc:
     return make_desc(w.tokens, w.hidden, w.inter, w.num_experts, w.topk, w.local_begin, w.num_local,
                      w.weight_format, w.activation, w.act_clamp, w.act_alpha, w.act_up_bias, variant,
-                     getattr(w, "scaling", "block"), getattr(w, "h_scale", 1.0), getattr(w, "num_shared", 0))
+                     getattr(w, "scaling", "block"), getattr(w, "h_scale", 1.0), getattr(w, "num_shared", 0),
+                     scale_layout)
 
 
 def moe_workspace_size(desc: MoeLayerDesc) -> int:

@@ -109,6 +109,10 @@ struct GemmArgs {
   uint8_t* h;            // FC1 out
   uint8_t* h_sf;
   float* y2;             // FC2 out
+  // packed int32 MN-major activation scales (0: row-major bytes): aligned row counts of the A
+  // operand's scale tensor and of the FC1 output h_sf; the byte of (row, group g) is at
+  // ((g / 4) * aligned + row) * 4 + g % 4
+  int asf_am, hsf_am;
   long long b_estride;   // bytes per expert of B
   long long bsf_estride; // bytes per expert of B_sf
   int K;                 // contraction length (H for FC1, I for FC2)
@@ -349,7 +353,8 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   __syncthreads();
   // activation scales of the tile rows in LDS as [row][k step]: moved by 4-byte DMA when a
   // row is whole dwords (nk128 % 4 == 0), else by byte loads
-  const uint8_t* asf_gbase = MODE == 1 ? g.A_sf : g.A_sf + (long long)row_begin * nk128;
+  const bool asf_packed = g.asf_am > 0;
+  const uint8_t* asf_gbase = MODE == 1 || asf_packed ? g.A_sf : g.A_sf + (long long)row_begin * nk128;
   const bool asf_dma = !C::BF16 && !g.tensor && (nk128 & 3) == 0 && ((BM * nk128) & 255) == 0;
   constexpr int kAsfDma = (BM * kMaxKSteps / 256 + NW - 1) / NW;  // 64-lane DMAs per wave, at most
   const int asf_n = BM * nk128 / 256;                               // 64-lane DMAs of the tile
@@ -359,12 +364,17 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
 #pragma unroll
     for (int j = 0; j < kAsfDma; ++j) {
       const int q = (wave + NW * j) * 64 + lane, row = min(q / dpr, BM - 1);
-      asf_off[j] = (uint32_t)(s_tok[row] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)nk128 + (uint32_t)(q - row * dpr) * 4u;
+      asf_off[j] = asf_packed ? ((uint32_t)(q - row * dpr) * (uint32_t)g.asf_am + (uint32_t)s_tok[row]) * 4u
+                              : (uint32_t)(s_tok[row] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)nk128 +
+                                    (uint32_t)(q - row * dpr) * 4u;
     }
   } else if (!C::BF16) {
     for (int i = tid; i < nk128 * BM; i += C::NTHR) {
       const int r = i / nk128;
-      s_asf[i] = g.tensor ? 127 : asf_gbase[(long long)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * nk128 + (i - r * nk128)];
+      const int ks = i - r * nk128;
+      s_asf[i] = g.tensor ? 127
+                 : asf_packed ? asf_gbase[((long long)(ks >> 2) * g.asf_am + s_tok[r]) * 4 + (ks & 3)]
+                              : asf_gbase[(long long)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * nk128 + ks];
     }
   }
 
@@ -813,7 +823,11 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     if (r < rows) {
       *reinterpret_cast<uint4*>(g.h + (long long)(row_begin + r) * g.I + n0 + c * 16) =
           *reinterpret_cast<const uint4*>(stage_h + r * 128 + ((c ^ (r & 7)) << 4));
-      if (c == 0 && !g.tensor) g.h_sf[(long long)(row_begin + r) * (g.I / 128) + n_tile] = stage_sf[r];
+      if (c == 0 && !g.tensor) {
+        const long long at = g.hsf_am > 0 ? ((long long)(n_tile >> 2) * g.hsf_am + row_begin + r) * 4 + (n_tile & 3)
+                                          : (long long)(row_begin + r) * (g.I / 128) + n_tile;
+        g.h_sf[at] = stage_sf[r];
+      }
     }
   }
 }
@@ -925,6 +939,10 @@ hipError_t launch_fc1(const Shape& sh, int variant, int variant_shared, const ui
                 : sh.wfmt != 1 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
   a.act = sh.act; a.clamp = sh.clamp; a.alpha = sh.alpha; a.bias = sh.bias;
+  if (sh.sf_packed) {
+    a.asf_am = (sh.T + 3) & ~3;
+    a.hsf_am = (sh.T * (sh.k + sh.S) + 3) & ~3;
+  }
   set_tensor_scales(a, sh, reinterpret_cast<const float*>(x_sf), reinterpret_cast<const float*>(w1_sf));
   const bool split = sh.S > 0 && variant_shared != variant;
   // routed experts (and the shared ones unless they take their own launch); the permute's tile
@@ -958,6 +976,7 @@ hipError_t launch_fc2(const Shape& sh, int variant, int variant_shared, const ui
   a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.T = sh.T;
   a.b_estride = sh.wfmt == 3 ? (long long)sh.H * sh.I * 2 : sh.wfmt != 1 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
+  if (sh.sf_packed) a.asf_am = (sh.T * (sh.k + sh.S) + 3) & ~3;
   set_tensor_scales(a, sh, nullptr, reinterpret_cast<const float*>(w2_sf));
   const bool split = sh.S > 0 && variant_shared != variant;
   a.routed = 1;

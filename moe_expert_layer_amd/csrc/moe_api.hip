@@ -72,7 +72,9 @@ Layout make_layout(const moe_layer_desc& d) {
   L.plan1 = take(NB * 4);
   const size_t hrows = cap + (size_t)d.num_shared * d.num_tokens;  // routed rows, then shared experts' rows
   L.h = take(hrows * (size_t)d.inter * (d.weight_format == MOE_W_BF16 ? 2 : 1));
-  L.h_sf = take(hrows * (size_t)(d.inter / 128));
+  // row-major bytes, or packed int32 words [ceil(groups / 4)][rows rounded up to 4]
+  L.h_sf = take(d.scale_layout == MOE_SF_PACKED_MN ? (size_t)4 * ((d.inter / 128 + 3) / 4) * ((hrows + 3) / 4 * 4)
+                                                    : hrows * (size_t)(d.inter / 128));
   L.y2 = take(hrows * (size_t)d.hidden * 4);
   L.total = at;
   return L;
@@ -118,6 +120,10 @@ moe_status check_desc(const moe_layer_desc* d) {
     if (!std::isfinite(d->h_scale) || !(d->h_scale > 0.f))
       return fail(MOE_ERR_INVALID_DESC, "h_scale must be finite and > 0");
   }
+  if (d->scale_layout != MOE_SF_ROW_MAJOR && d->scale_layout != MOE_SF_PACKED_MN)
+    return fail(MOE_ERR_INVALID_DESC, "scale_layout %d unknown", d->scale_layout);
+  if (d->scale_layout == MOE_SF_PACKED_MN && (d->scale_mode != MOE_SCALE_BLOCK || d->weight_format == MOE_W_BF16))
+    return fail(MOE_ERR_INVALID_DESC, "packed scale layout needs blockwise UE8M0 scales");
   if (!moe::gemm_supports(d->hidden, d->inter))
     return fail(MOE_ERR_UNSUPPORTED, "hidden %d / inter %d above the supported 8192", d->hidden, d->inter);
   const long long x_bytes = (long long)d->num_tokens * d->hidden * (d->weight_format == MOE_W_BF16 ? 2 : 1);
@@ -178,6 +184,7 @@ moe::Shape shape_of(const moe_layer_desc& d) {
   s.EL = d.num_local; s.k = d.topk; s.wfmt = d.weight_format; s.act = d.activation;
   s.S = d.num_shared;
   s.exact_fc1 = exact_fc1(d);
+  s.sf_packed = d.scale_layout == MOE_SF_PACKED_MN;
   s.tensor = d.scale_mode == MOE_SCALE_TENSOR;
   s.h_scale = s.tensor ? d.h_scale : 1.f;
   if (d.activation == MOE_ACT_SWIGLU_OAI) {
@@ -262,6 +269,7 @@ moe_status moe_desc_defaults(moe_layer_desc* d) {
   d->variant = -1;
   d->scale_mode = MOE_SCALE_BLOCK;
   d->h_scale = 1.0f;
+  d->scale_layout = MOE_SF_ROW_MAJOR;
   return ok();
 }
 

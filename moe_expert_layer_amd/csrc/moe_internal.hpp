@@ -22,6 +22,7 @@ struct Shape {
   bool tensor = false;  // per-tensor float32 scales instead of UE8M0 blocks
   float h_scale = 1.f;  // per-tensor: static scale of the intermediate
   bool exact_fc1 = false;  // FC1 sums through BF16 MFMAs on operands converted in registers
+  bool sf_packed = false;  // x_sf and h_sf are packed int32 MN-major (aligned rows T and T*(k+S))
   int act;   // 0 swiglu, 1 oai
   float clamp, alpha, bias;
 };

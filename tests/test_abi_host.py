@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(L, header):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert B.status_str(0) == "MOE_OK" and B.status_str(5) == "MOE_ERR_WORKSPACE"
     assert B.status_str(99) == "MOE_STATUS_UNKNOWN"
 
@@ -55,7 +55,7 @@ def test_defaults_follow_standard_swiglu(L):
     assert L.moe_desc_defaults(ctypes.byref(d)) == 0
     assert d.activation == B.MOE_ACT_SWIGLU and d.weight_format == B.MOE_W_FP8_E4M3_B128
     assert math.isinf(d.act_clamp) and d.act_alpha == 1.0 and d.act_up_bias == 0.0 and d.variant == -1
-    assert d.scale_mode == B.MOE_SCALE_BLOCK and d.h_scale == 1.0
+    assert d.scale_mode == B.MOE_SCALE_BLOCK and d.h_scale == 1.0 and d.scale_layout == B.MOE_SF_ROW_MAJOR
 
 
 @pytest.mark.parametrize("i", range(5))

@@ -51,6 +51,15 @@ def _small_cases():
                                     num_local=8, topk=4, num_shared=1, seed=18)),
         ("shared2_partial", synth.shrink(tiny, tokens=40, hidden=512, inter=256, num_experts=64, local_begin=10,
                                          num_local=8, topk=4, num_shared=2, seed=19)),
+        # shared experts whose exact row count (every token) picks another tile shape than the
+        # routed experts' heuristic: routed 32-row tiles with 128-row shared tiles (the decode
+        # regime; MXFP4 with two shared experts), routed 32-row with 256-row shared tiles
+        ("shared_tiles_v2_v0", synth.shrink(tiny, tokens=100, hidden=512, inter=256, num_experts=64, local_begin=8,
+                                            num_local=16, topk=4, num_shared=1, seed=34)),
+        ("shared_tiles_v2_v0_mxfp4", synth.shrink(synth.workload("mxfp4_large"), tokens=90, hidden=512, inter=384,
+                                                  num_experts=64, num_local=16, topk=4, num_shared=2, seed=35)),
+        ("shared_tiles_v2_v1", synth.shrink(oai, tokens=300, hidden=512, inter=256, num_experts=64, num_local=32,
+                                            topk=4, num_shared=1, seed=36)),
         # the whole layer in bfloat16 (x, weights, h), with a shared expert in the second case
         ("bf16_oai", synth.shrink(oai, tokens=300, hidden=768, inter=384, num_experts=16, local_begin=2,
                                   num_local=8, topk=4, weight_format="bf16", seed=25)),
