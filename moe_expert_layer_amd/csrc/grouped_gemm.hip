@@ -231,6 +231,34 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ plan, int
   return lo;
 }
 
+// FC2 epilogue: fp32 rows of Y2 from the accumulators (tokens are the MFMA's first operand:
+// lane l of acc[mi][ct] holds rows 8*(i/4) + 4*kb + i%4 of row tile mi, column
+// bcol(ct) + l%32), 32 consecutive columns per lane group.  The 256-row tiles (shares with
+// hundreds of MB of Y2) store non-temporally so the burst does not evict the operands; the
+// smaller tiles' Y2 (tens of MB) stays in the caches for the combine, which reads it next.
+template <int BM, int BN, int WTM, int WM, int WN, int MI, int NT>
+__device__ __forceinline__ void store_y2_rows(float* __restrict__ y2, int N, const v16f (&acc)[MI][NT], int wave,
+                                              int lane, int rb, int nrows, int c0) {
+  const int wm = wave % WM, wn = wave / WM;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (r < nrows) {
+        float* dst = y2 + (long long)(rb + r) * N;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const int col = c0 + wn * (BN / WN) + ct * 32 + (lane & 31);
+          if (col < N) {
+            if constexpr (BM == 256) __builtin_nontemporal_store(acc[mi][ct][i], dst + col);
+            else dst[col] = acc[mi][ct][i];
+          }
+        }
+      }
+    }
+}
+
 // Two workgroups per CU for the tiles whose ring fits twice in LDS (the register budget
 // follows from that); one otherwise.
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
@@ -244,11 +272,19 @@ constexpr int kWgPerCu = NSTAGE * Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, P
 // bits) and multiplies with the BF16 MFMA, whose fp32 sums match a sequential fp32 sum of the
 // exact products.  It costs conversion instructions and half the matrix-core rate, which is
 // free where the GEMM streams weights (few rows per expert).
-template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE, int XA>
+//
+// PT (FC2 only): persistent workgroups.  Each workgroup walks its XCD's tile range with a stride
+// of the workgroups on that XCD, and stores a tile's Y2 rows only after it has issued the next
+// tile's first DMA stages, so the store burst at the end of a tile overlaps the next tile's
+// operand loads instead of idling the matrix cores.  The tile plan then lives outside the
+// stage ring, and the stores precede the DMAs in issue order, so every stage wait (which counts
+// outstanding vector memory operations in issue order) also covers them.
+template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE, int XA, int PT>
 __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>)) void grouped_gemm_kernel(
     GemmArgs g) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   static_assert(!XA || (MODE == 1 && WFMT != 3), "exact-sum FC1 is for the scaled formats");
+  static_assert(!PT || MODE == 2, "persistent workgroups are for FC2");
   using F = Frags<C::MI, C::NT, C::NH>;
   // LDS (dynamic, sized at launch): the stage ring, then the tile's activation scales
   // [row][ks128] and FP8 weight scales [block][ks128].  The token list of the tile rows and
@@ -266,7 +302,8 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   // scans the offsets itself.  Either way the plan and the expert offsets are put in LDS
   // (inside the ring, which the prologue does not use yet) by loads that are all in flight
   // together, so the expert search below reads LDS instead of chaining dependent global loads
-  int* s_plan = reinterpret_cast<int*>(ring);  // [EL + S + 1]
+  int* s_plan = PT ? reinterpret_cast<int*>(lds + ((NSTAGE * C::STAGE + (BM + 2) * nk128_ + 15) & ~15))
+                   : reinterpret_cast<int*>(ring);  // [EL + S + 1]
   int* s_wsum = s_plan + kMaxExperts + 8;      // [NW]
   int* s_offs = s_wsum + 16;                   // [EL + 1]
   static_assert(NSTAGE * C::STAGE >= (2 * kMaxExperts + 32) * 4 + BM * 4, "plan and offsets fit before s_tok");
@@ -300,12 +337,27 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   const int NE = g.EL + g.S;  // experts with rows: routed, then shared
   const int total = plan[NE] * g.n_tiles;
   const int bid = blockIdx.x;
-  if (bid >= total) return;
-  int L;  // XCD-aware order: dispatch is round-robin over 8 XCDs; each XCD gets a contiguous range
+  // XCD-aware order: dispatch is round-robin over 8 XCDs; each XCD gets a contiguous range of
+  // tiles (persistent: workgroup bid >> 3 of XCD bid & 7 takes every (gridDim.x / 8)-th of them)
+  int L, pt_p = 0, pt_cnt = 0, pt_base = 0;
   {
-    const int x = bid & 7, p = bid >> 3, q = total >> 3, r = total & 7;
-    L = x * q + (x < r ? x : r) + p;
+    const int x = bid & 7, q = total >> 3, r = total & 7;
+    pt_p = bid >> 3;
+    pt_cnt = q + (x < r ? 1 : 0);
+    pt_base = x * q + (x < r ? x : r);
+    if (pt_p >= pt_cnt) return;
+    L = pt_base + pt_p;
   }
+  // FC2 epilogue: fp32 rows of Y2 from the accumulators (tokens are the MFMA's first operand:
+  // lane l of acc[mi][ct] holds rows 8*(i/4) + 4*kb + i%4 of row tile mi, column
+  // bcol(ct) + l%32), 32 consecutive columns per lane group.  The 256-row tiles (shares with
+  // hundreds of MB of Y2) store non-temporally so the burst does not evict the operands; the
+  // smaller tiles' Y2 (tens of MB) stays in the caches for the combine, which reads it next
+  v16f acc[C::MI][C::NT];
+  int pv_row_begin = 0, pv_rows = 0, pv_n0 = 0;  // the tile whose Y2 stores are pending (PT)
+  bool pv_live = false, pv_have = false;
+  for (;;) {
+  if (PT && pv_have) __syncthreads();  // every wave is past its last LDS read of the previous tile
   const int e = find_expert(plan, NE, L / g.n_tiles);
   const int mt_e = plan[e + 1] - plan[e];
   const int li = L - plan[e] * g.n_tiles;
@@ -412,6 +464,9 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   // every wave, scale lanes or not: no load of the compiler's own is outstanding past this
   // point, so it adds no vmcnt(0) (which would also drain the DMAs) for this load's register
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited for
+  // persistent FC2: the previous tile's Y2 stores go out now, ahead of this tile's DMAs
+  if (PT && pv_have && pv_live)
+    store_y2_rows<BM, BN, WTM, C::WM, C::WN, C::MI, C::NT>(g.y2, g.N, acc, wave, lane, pv_row_begin, pv_rows, pv_n0);
   if (asf_dma) {
 #pragma unroll
     for (int j = 0; j < kAsfDma; ++j)
@@ -439,7 +494,6 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     else wait_vm_barrier<0>();
   };
 
-  v16f acc[C::MI][C::NT];
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -666,31 +720,16 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   }
 
   if (MODE == 2) {
-    // ---- FC2 epilogue (tokens are the MFMA's first operand: lane l of acc[mi][ct] holds
-    //      rows 8*(i/4) + 4*kb + i%4 of row tile mi, column bcol(ct) + l%32): fp32 rows of Y2,
-    //      32 consecutive columns per lane group.  The 256-row tiles (shares with hundreds of
-    //      MB of Y2) store non-temporally so the burst at the end of the tiles does not evict
-    //      the operands; the smaller tiles' Y2 (tens of MB) stays in the caches for the
-    //      combine, which reads it next ----
-    if (wave_live) {
-#pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = wm * WTM + mi * 32 + 8 * (i >> 2) + 4 * kb + (i & 3);
-          if (r < rows) {
-            float* dst = g.y2 + (long long)(row_begin + r) * g.N;
-#pragma unroll
-            for (int ct = 0; ct < C::NT; ++ct) {
-              const int col = n0 + bcol(ct) + lrow;
-              if (col < g.N) {
-                if constexpr (BM == 256) __builtin_nontemporal_store(acc[mi][ct][i], dst + col);
-                else dst[col] = acc[mi][ct][i];
-              }
-            }
-          }
-        }
+    if (PT) {  // the next tile of this workgroup, if any; this tile's stores are deferred
+      pv_row_begin = row_begin; pv_rows = rows; pv_n0 = n0; pv_live = wave_live; pv_have = true;
+      pt_p += gridDim.x >> 3;
+      if (pt_p < pt_cnt) {
+        L = pt_base + pt_p;
+        continue;
+      }
     }
+    if (wave_live)
+      store_y2_rows<BM, BN, WTM, C::WM, C::WN, C::MI, C::NT>(g.y2, g.N, acc, wave, lane, row_begin, rows, n0);
     return;
   }
 
@@ -830,6 +869,8 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
       }
     }
   }
+  return;
+  }  // tile loop
 }
 
 // variant 0: 128-row tiles, 4 waves (FC1: 64-K stages x 3, FC2: 128 columns, 128-K stages
@@ -851,14 +892,29 @@ size_t gemm_max_mtiles(int rows_cap, int EL, int variant, int T, int S) {
 
 bool gemm_supports(int H, int I) { return H / 128 <= kMaxKSteps && I / 128 <= kMaxKSteps; }
 
-template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE, int XA>
+// compute units of the current device (cached per device)
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE, int XA, int PT = 0>
 static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   using C = Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>;
   static_assert(NSTAGE * C::STAGE >= BM * 128 + C::WN * BM * 4 + BM && NSTAGE * C::STAGE >= BM * 4 + BM * 128 &&
                     (!C::BF16 || NSTAGE * C::STAGE >= BM * 256),
                 "the ring must hold the epilogue staging and the tile's token list");
-  auto kern = grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE, XA>;
-  const size_t lds = (size_t)NSTAGE * C::STAGE + (size_t)BM * (a.K / 128) + 2 * (a.K / 128);
+  auto kern = grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE, XA, PT>;
+  constexpr size_t kPlanBytes = (2 * kMaxExperts + 32) * 4;  // persistent: plan, block sums, offsets
+  const size_t nk128 = C::BF16 ? 0 : a.K / 128;
+  const size_t lds = PT ? (((size_t)NSTAGE * C::STAGE + (BM + 2) * nk128 + 15) & ~(size_t)15) + kPlanBytes
+                        : (size_t)NSTAGE * C::STAGE + (size_t)BM * (a.K / 128) + 2 * (a.K / 128);
   // raise the kernel's dynamic LDS limit to its largest size (K = 8192) once per device
   static std::atomic<uint64_t> ready{0};
   int dev = 0;
@@ -866,10 +922,14 @@ static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(ready.load(std::memory_order_acquire) & bit)) {
-    const size_t most = (size_t)NSTAGE * C::STAGE + (size_t)(BM + 2) * kMaxKSteps;
+    const size_t most = (size_t)NSTAGE * C::STAGE + (size_t)(BM + 2) * kMaxKSteps + (PT ? 16 + kPlanBytes : 0);
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
     if (e != hipSuccess) return e;
     ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  if (PT) {  // one workgroup per CU (rounded to whole XCD rows of 8), or fewer for a small grid
+    const size_t cus = (size_t)device_cus();
+    grid = ((grid < cus ? grid : cus) + 7) / 8 * 8;
   }
   kern<<<dim3((unsigned)grid), dim3(NW * 64), lds, s>>>(a);
   return hipGetLastError();
@@ -882,6 +942,7 @@ static hipError_t launch_variant_w(const GemmArgs& a, int variant, size_t grid, 
   // AGPRs (measured on the 32768-token share: 0.941 against 0.977 ms)
   if (variant == 1) {
     if constexpr (MODE == 1 && WFMT == 1) return launch_one<MODE, WFMT, 256, 256, 128, 2, 4, 128, 2, XA>(a, grid, s);
+    else if constexpr (MODE == 2) return launch_one<MODE, WFMT, 256, 256, 128, 2, 8, 64, 2, XA, 1>(a, grid, s);
     else return launch_one<MODE, WFMT, 256, 256, 128, 2, 8, 64, 2, XA>(a, grid, s);
   }
   if (variant == 2) {
