@@ -121,7 +121,6 @@ struct GemmArgs {
   int k;                 // top-k (FC1 row -> token)
   int EL;                // routed local experts; shared experts EL .. EL + S - 1 follow them
   int S;                 // shared experts: each has the T rows [offsets[EL] + s T, + T), one per token
-  int routed;            // 1: the routed experts' rows are tiled too; 0: this launch tiles the shared experts only
   int T;
   int n_tiles;
   int act;
@@ -321,7 +320,7 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     for (int j = 0; j < per; ++j) {
       const int ee = beg + j;
       if (ee < n) s_plan[ee] = sum;
-      if (ee < g.EL) sum += g.routed ? (g.offsets[ee + 1] - g.offsets[ee] + BM - 1) / BM : 0;
+      if (ee < g.EL) sum += (g.offsets[ee + 1] - g.offsets[ee] + BM - 1) / BM;
       else if (ee < n - 1) sum += (g.T + BM - 1) / BM;
     }
     const int inc = wave_inclusive_scan(sum);
@@ -986,16 +985,14 @@ static void set_tensor_scales(GemmArgs& a, const Shape& sh, const float* a_scale
   a.h_inv = 1.0f / sh.h_scale;
 }
 
-// Shared experts have exactly T rows each, known on the host, so they may use another tile shape
-// than the routed experts (variant_shared); then the routed and the shared experts' tiles are two
-// launches of the same kernel family, the second with its tile plan over the shared experts only.
-hipError_t launch_fc1(const Shape& sh, int variant, int variant_shared, const uint8_t* x, const uint8_t* x_sf,
-                      const uint8_t* w1, const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot,
-                      uint8_t* h, uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s) {
+hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
+                      const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
+                      uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s) {
   GemmArgs a{};
   a.A = x; a.A_sf = x_sf; a.row_to_slot = row_to_slot; a.B = w1; a.B_sf = w1_sf;
-  a.offsets = offsets; a.h = h; a.h_sf = h_sf;
-  a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.T = sh.T; a.n_tiles = sh.I / 128;
+  // the permute's tile plan covers the routed experts only
+  a.offsets = offsets; a.plan = plan_ready && sh.S == 0 ? plan : nullptr; a.h = h; a.h_sf = h_sf;
+  a.K = sh.H; a.N = 2 * sh.I; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.S = sh.S; a.T = sh.T; a.n_tiles = sh.I / 128;
   a.b_estride = sh.wfmt == 3 ? (long long)2 * sh.I * sh.H * 2
                 : sh.wfmt != 1 ? (long long)2 * sh.I * sh.H : (long long)2 * sh.I * sh.H / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(2 * sh.I / 128) * (sh.H / 128) : (long long)2 * sh.I * (sh.H / 32);
@@ -1005,61 +1002,30 @@ hipError_t launch_fc1(const Shape& sh, int variant, int variant_shared, const ui
     a.hsf_am = (sh.T * (sh.k + sh.S) + 3) & ~3;
   }
   set_tensor_scales(a, sh, reinterpret_cast<const float*>(x_sf), reinterpret_cast<const float*>(w1_sf));
-  const bool split = sh.S > 0 && variant_shared != variant;
-  // routed experts (and the shared ones unless they take their own launch); the permute's tile
-  // plan covers the routed experts only
-  a.routed = 1;
-  a.S = split ? 0 : sh.S;
-  a.plan = plan_ready && a.S == 0 ? plan : nullptr;
-  size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, a.S) * (size_t)a.n_tiles;
+  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, sh.S) * (size_t)a.n_tiles;
+  if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (grid > 0) {
-    const hipError_t e = launch_variant<1>(a, sh.wfmt, variant, sh.exact_fc1, grid, s);
-    if (e != hipSuccess || !split) return e;
-  } else if (!split) {
-    return hipSuccess;
-  }
-  a.routed = 0;
-  a.S = sh.S;
-  a.plan = nullptr;
-  const int bm = gemm_block_m(variant_shared);
-  grid = (size_t)sh.S * (((size_t)sh.T + bm - 1) / bm) * (size_t)a.n_tiles;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  return launch_variant<1>(a, sh.wfmt, variant_shared, sh.exact_fc1, grid, s);
+  return launch_variant<1>(a, sh.wfmt, variant, sh.exact_fc1, grid, s);
 }
 
-hipError_t launch_fc2(const Shape& sh, int variant, int variant_shared, const uint8_t* h, const uint8_t* h_sf,
-                      const uint8_t* w2, const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan,
-                      bool plan_ready, hipStream_t s) {
+hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
+                      const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, bool plan_ready,
+                      hipStream_t s) {
   GemmArgs a{};
   a.A = h; a.A_sf = h_sf; a.B = w2; a.B_sf = w2_sf; a.offsets = offsets;
+  a.plan = plan_ready && sh.S == 0 ? plan : nullptr;
   a.y2 = y2;
-  a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.T = sh.T;
+  a.K = sh.I; a.N = sh.H; a.I = sh.I; a.k = sh.k; a.EL = sh.EL; a.S = sh.S; a.T = sh.T;
   a.b_estride = sh.wfmt == 3 ? (long long)sh.H * sh.I * 2 : sh.wfmt != 1 ? (long long)sh.H * sh.I : (long long)sh.H * sh.I / 2;
   a.bsf_estride = sh.wfmt != 1 ? (long long)(sh.H / 128) * (sh.I / 128) : (long long)sh.H * (sh.I / 32);
   if (sh.sf_packed) a.asf_am = (sh.T * (sh.k + sh.S) + 3) & ~3;
   set_tensor_scales(a, sh, nullptr, reinterpret_cast<const float*>(w2_sf));
-  const bool split = sh.S > 0 && variant_shared != variant;
-  a.routed = 1;
-  a.S = split ? 0 : sh.S;
-  a.plan = plan_ready && a.S == 0 ? plan : nullptr;
-  a.n_tiles = (sh.H + (variant == 0 ? 128 : 256) - 1) / (variant == 0 ? 128 : 256);
-  size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, a.S) * (size_t)a.n_tiles;
+  const int bn = variant == 0 ? 128 : 256;
+  a.n_tiles = (sh.H + bn - 1) / bn;
+  const size_t grid = gemm_max_mtiles(sh.T * sh.k, sh.EL, variant, sh.T, sh.S) * (size_t)a.n_tiles;
+  if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (grid > 0) {
-    const hipError_t e = launch_variant<2>(a, sh.wfmt, variant, false, grid, s);
-    if (e != hipSuccess || !split) return e;
-  } else if (!split) {
-    return hipSuccess;
-  }
-  a.routed = 0;
-  a.S = sh.S;
-  a.plan = nullptr;
-  a.n_tiles = (sh.H + (variant_shared == 0 ? 128 : 256) - 1) / (variant_shared == 0 ? 128 : 256);
-  const int bm = gemm_block_m(variant_shared);
-  grid = (size_t)sh.S * (((size_t)sh.T + bm - 1) / bm) * (size_t)a.n_tiles;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  return launch_variant<2>(a, sh.wfmt, variant_shared, false, grid, s);
+  return launch_variant<2>(a, sh.wfmt, variant, false, grid, s);
 }
 
 }  // namespace moe

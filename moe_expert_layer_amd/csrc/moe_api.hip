@@ -208,15 +208,6 @@ int pick_variant(const moe_layer_desc& d) {
   return 0;
 }
 
-// Tile variant of the shared experts: each has exactly T rows, which the host knows, so the
-// same thresholds as above apply to T itself (a forced variant applies to every expert).
-int pick_shared_variant(const moe_layer_desc& d) {
-  if (d.variant >= 0) return d.variant;
-  if (d.num_tokens >= 256) return 1;
-  if (d.num_tokens <= 48) return 2;
-  return 0;
-}
-
 #define MOE_TRY_HIP(call)                                                            \
   do {                                                                               \
     hipError_t e_ = (call);                                                          \
@@ -309,7 +300,7 @@ moe_status moe_grouped_fc1_swiglu(const moe_layer_desc* d, const uint8_t* x, con
   if (moe_status st = check_ws(d, ws, ws_bytes)) return st;
   if (moe_status st = check_device()) return st;
   const moe::Shape sh = shape_of(*d);
-  MOE_TRY_HIP(moe::launch_fc1(sh, pick_variant(*d), pick_shared_variant(*d), x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
+  MOE_TRY_HIP(moe::launch_fc1(sh, pick_variant(*d), x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
                               nullptr, false, (hipStream_t)stream));
   return ok();
 }
@@ -330,7 +321,7 @@ moe_status moe_grouped_fc2_combine(const moe_layer_desc* d, const uint8_t* h, co
   const Layout L = make_layout(*d);
   const moe::Shape sh = shape_of(*d);
   float* y2 = region<float>(ws, L.y2);
-  MOE_TRY_HIP(moe::launch_fc2(sh, pick_variant(*d), pick_shared_variant(*d), h, h_sf, w2, w2_sf, offsets, y2, nullptr,
+  MOE_TRY_HIP(moe::launch_fc2(sh, pick_variant(*d), h, h_sf, w2, w2_sf, offsets, y2, nullptr,
                               false, (hipStream_t)stream));
   MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, offsets + d->num_local,
                                   d->num_shared, y, (hipStream_t)stream));
@@ -372,11 +363,9 @@ moe_status run_layer(const moe_layer_desc* d, const float* logits, const uint8_t
   const int variant = pick_variant(*d);
   if (moe_status st = run_route_permute(*d, L, logits, ids, w, counts, offsets, r2s, s2r, ws, s)) return st;
   // the permute wrote the tile plan of these offsets (plan1) for this variant's tile rows
-  const int variant_shared = pick_shared_variant(*d);
-  MOE_TRY_HIP(moe::launch_fc1(sh, variant, variant_shared, x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
+  MOE_TRY_HIP(moe::launch_fc1(sh, variant, x, x_sf, w1, w1_sf, offsets, r2s, h, h_sf,
                               region<int32_t>(ws, L.plan1), true, s));
-  MOE_TRY_HIP(moe::launch_fc2(sh, variant, variant_shared, h, h_sf, w2, w2_sf, offsets, y2,
-                              region<int32_t>(ws, L.plan1), true, s));
+  MOE_TRY_HIP(moe::launch_fc2(sh, variant, h, h_sf, w2, w2_sf, offsets, y2, region<int32_t>(ws, L.plan1), true, s));
   MOE_TRY_HIP(moe::launch_combine(y2, s2r, w, d->num_tokens, d->hidden, d->topk, offsets + d->num_local,
                                   d->num_shared, y, s));
   return ok();

@@ -44,12 +44,10 @@ size_t gemm_max_mtiles(int rows_cap, int EL, int variant, int T, int S);
 // plan_ready: `plan` holds the tile plan of these offsets for this variant's tile rows (written
 // by launch_permute); otherwise `plan` is ignored and every GEMM workgroup derives the plan
 // from `offsets` in its prologue.
-// variant_shared: tile variant of the shared experts (their tiles take a launch of their own
-// when it differs from the routed experts' variant)
-hipError_t launch_fc1(const Shape& sh, int variant, int variant_shared, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
+hipError_t launch_fc1(const Shape& sh, int variant, const uint8_t* x, const uint8_t* x_sf, const uint8_t* w1,
                       const uint8_t* w1_sf, const int32_t* offsets, const int32_t* row_to_slot, uint8_t* h,
                       uint8_t* h_sf, int32_t* plan, bool plan_ready, hipStream_t s);
-hipError_t launch_fc2(const Shape& sh, int variant, int variant_shared, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
+hipError_t launch_fc2(const Shape& sh, int variant, const uint8_t* h, const uint8_t* h_sf, const uint8_t* w2,
                       const uint8_t* w2_sf, const int32_t* offsets, float* y2, int32_t* plan, bool plan_ready,
                       hipStream_t s);
 
