@@ -118,8 +118,10 @@ def pct(a, b):
 
 
 def run_probes(torch, steps=5):
-    """Achievable matrix-core rate (FP8 x FP8 and FP8 x FP4 scaled 32x32x64 MFMA loops) and HBM read
-    bandwidth (a 4 GiB streaming read), each the best of `steps` timed runs."""
+    """Achievable matrix-core rate (FP8 x FP8 and FP8 x FP4 scaled 32x32x64 MFMA loops), HBM read
+    bandwidth (a 4 GiB streaming read) and the per-CU rate of the GEMMs' operand stream (direct
+    global-to-LDS loads of 512-row panels, from HBM and from L2-resident panels, one or two 64 KB
+    stages in flight), each the best of `steps` timed runs."""
     from moe_expert_layer_amd import probe_binding as PB
     props = torch.cuda.get_device_properties(0)
     cus = props.multi_processor_count
@@ -159,6 +161,27 @@ def run_probes(torch, steps=5):
     gbs = nbytes / (best * 1e-3) / 1e9
     out["hbm_read"] = {"gbs": round(gbs, 1), "published_gbs": PEAK_HBM_GBS, "frac_of_published": round(gbs / PEAK_HBM_GBS, 4),
                        "bytes": nbytes}
+    del sink
+    # the GEMMs' operand stream without arithmetic: one 512-thread workgroup per CU streaming
+    # 512-row panels into a two-stage ring of 64 KB LDS stages (per-CU load-path rate)
+    sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    for name, K, panels, passes in (("dma_stream_hbm", 7168, 0, 1), ("dma_stream_l2", 2048, 8, 16)):
+        for depth in (1, 2):
+            PB.dma_stream(src, K, cus, panels, 1, depth, sink)
+            best = None
+            for _ in range(steps):
+                torch.cuda.synchronize()
+                e0.record()
+                PB.dma_stream(src, K, cus, panels, passes, depth, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1)
+                best = ms if best is None else min(best, ms)
+            moved = cus * passes * 512 * K
+            out[f"{name}_depth{depth}"] = {"gbs": round(moved / (best * 1e-3) / 1e9, 1),
+                                           "gbs_per_cu": round(moved / (best * 1e-3) / 1e9 / cus, 2),
+                                           "bytes_per_clk_per_cu_at_2p4ghz": round(moved / (best * 1e-3) / cus / 2.4e9, 2),
+                                           "bytes": moved}
     del src, sink
     torch.cuda.empty_cache()
     return out

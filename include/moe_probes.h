@@ -9,7 +9,11 @@
  *     form, to compare against an exact host dot product (accumulation precision);
  *   - moe_probe_mfma_loop: a timed loop of independent FP8 matrix instructions
  *     (achievable matrix-core rate);
- *   - moe_probe_hbm_read: a timed streaming read (achievable HBM read bandwidth).
+ *   - moe_probe_hbm_read: a timed streaming read (achievable HBM read bandwidth);
+ *   - moe_probe_dma_stream: the grouped GEMMs' operand stream without their arithmetic
+ *     (direct global-to-LDS loads into a ring of 64 KB stages, per-CU load-path rate from
+ *     HBM or from L2-resident data);
+ *   - moe_probe_cvt_bf16: the scaled FP8 / FP4 -> BF16 conversions (exactness).
  * The pages this library follows define the efficiency yardstick as useful FLOPs over the
  * kernel's latency, against the chip's peak ("DSV4 o_proj: fuse fp8/UE8M0 quantize into
  * o_a proj", Description: SOL = 2*M*N*K / latency); the probes give the achievable side
@@ -62,6 +66,24 @@ int moe_probe_mfma_loop(int blocks, int iters, int b_fp4, float* sink, void* str
  * loads spread over `blocks` workgroups of 256 threads (grid-stride), and writes one
  * float per thread to sink [blocks * 256].  1 <= blocks <= 2^20. */
 int moe_probe_hbm_read(const void* src, size_t bytes, int blocks, float* sink, void* stream);
+
+/* Operand-stream probe: the load path of the grouped GEMMs without their arithmetic.  Each of
+ * `blocks` workgroups of 512 threads streams a panel of 512 rows of K bytes (row stride K)
+ * into a ring of two 64 KB LDS stages with 16-byte direct global-to-LDS loads, 128 bytes of
+ * every row per stage, `passes` times over the panel.  Before each stage is treated as consumed
+ * the workgroup waits for it to land and passes a barrier, as the GEMM K loop does.  depth
+ * (1 or 2) is the number of stages in flight while the workgroup waits.  The GEMM loop keeps one
+ * ahead, because a slot is refilled only after its fragments have been read.
+ *   panels = 0: workgroup b streams panel b, so src holds `blocks` panels (data from HBM or the
+ *     Infinity Cache, depending on the total size);
+ *   panels = n > 0: workgroup b streams panel b % n.  With n = 8, the 32 workgroups of an XCD
+ *     share one panel (dispatch is round-robin over the XCDs), which stays in that XCD's L2
+ *     after the first pass when 512 K fits there.
+ * One float per thread goes to sink [blocks * 512].  Bytes moved = blocks * passes * 512 * K.
+ * Limits: K a multiple of 128 in [128, 65536]; src_bytes >= (panels ? panels : blocks) * 512 * K;
+ * 1 <= blocks <= 65536; 0 <= panels <= blocks; 1 <= passes <= 65536; depth 1 or 2. */
+int moe_probe_dma_stream(const void* src, size_t src_bytes, int K, int blocks, int panels, int passes, int depth,
+                         float* sink, void* stream);
 
 /* Scaled conversion probe: out[i] = the BF16 bits the gfx950 scaled conversion instruction
  * gives for code i with scale 2^(scale_bytes[i/32] - 127), passed as the float whose bit

@@ -1,7 +1,8 @@
 """ctypes binding of the measurement probes in include/moe_probes.h (libmoe_probes.so).
 
 The probes are not part of the layer; the tests and the bench use them to measure the
-matrix instructions' accumulation precision and the achievable matrix-core and HBM rates.
+matrix instructions' accumulation precision, the achievable matrix-core and HBM rates, and the
+per-CU rate of the GEMMs' operand stream.
 """
 from __future__ import annotations
 
@@ -30,6 +31,8 @@ def lib():
         L.moe_probe_mfma_loop.argtypes = [I32, I32, I32, P, P]
         L.moe_probe_hbm_read.restype = I32
         L.moe_probe_hbm_read.argtypes = [P, ctypes.c_size_t, I32, P, P]
+        L.moe_probe_dma_stream.restype = I32
+        L.moe_probe_dma_stream.argtypes = [P, ctypes.c_size_t, I32, I32, I32, I32, I32, P, P]
         L.moe_probe_cvt_bf16.restype = I32
         L.moe_probe_cvt_bf16.argtypes = [I32, I32, P, P, P, P]
         _lib = L
@@ -61,6 +64,12 @@ def mfma_loop(blocks: int, iters: int, sink, b_fp4: bool = False, stream=None):
 def hbm_read(src, blocks: int, sink, stream=None):
     _check(lib().moe_probe_hbm_read(src.data_ptr(), src.numel() * src.element_size(), blocks, sink.data_ptr(),
                                     _stream(stream)), "moe_probe_hbm_read")
+
+
+def dma_stream(src, K: int, blocks: int, panels: int, passes: int, depth: int, sink, stream=None):
+    """Operand-stream probe: blocks x passes x 512 x K bytes into LDS (see include/moe_probes.h)."""
+    _check(lib().moe_probe_dma_stream(src.data_ptr(), src.numel() * src.element_size(), K, blocks, panels, passes,
+                                      depth, sink.data_ptr(), _stream(stream)), "moe_probe_dma_stream")
 
 
 def cvt_bf16(fmt: int, codes, scale_bytes, out, stream=None):

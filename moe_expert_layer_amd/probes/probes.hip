@@ -198,6 +198,54 @@ __global__ __launch_bounds__(256) void probe_hbm_read_kernel(const v4i_* __restr
   sink[(long long)blockIdx.x * 256 + threadIdx.x] = (float)(acc & 0xffff);
 }
 
+// direct global-to-LDS load of 16 bytes per lane: LDS address M0 + 16 * lane.  The base sits in
+// SGPRs (readfirstlane); a VMEM instruction that reads an SGPR written by a VALU instruction
+// needs 5 wait states in between, which the asm provides (s_mov + s_nop 3; this also covers
+// the wait between writing M0 and the load that reads it)
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const void* b = reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(b), "s"(lds)
+               : "memory", "m0");
+}
+
+// 64 KB stage t of the panel (bytes [128 (t mod K/128), +128) of its 512 rows) into ring slot
+// t % 2: wave w issues 8 loads, load j covering rows 64 w + 8 j .. +8 (8 lanes of 16 bytes a row)
+template <int DEPTH>
+__global__ __launch_bounds__(512) void probe_dma_stream_kernel(const uint8_t* __restrict__ src, int K, int panels,
+                                                               int passes, float* __restrict__ sink) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t ring[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int panel = panels ? (int)(blockIdx.x % panels) : (int)blockIdx.x;
+  const uint8_t* base = src + (size_t)panel * 512 * (size_t)K;
+  uint32_t off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) off[j] = (uint32_t)((wave * 64 + j * 8 + (lane >> 3)) * K + (lane & 7) * 16);
+  const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
+  const int nk = K / 128, total = passes * nk;
+  auto issue = [&](int t) {
+    const uint8_t* b = base + (size_t)(t % nk) * 128;
+    const uint32_t st = ring0 + (uint32_t)((t & 1) * 65536 + wave * 8192);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(b, off[j], __builtin_amdgcn_readfirstlane(st + j * 1024));
+  };
+  issue(0);
+  if (DEPTH == 2 && total > 1) issue(1);
+  for (int t = 0; t < total; ++t) {
+    if (DEPTH == 1) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // stage t landed everywhere
+      if (t + 1 < total) issue(t + 1);
+    } else {
+      if (t + 1 < total) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");  // t landed, t + 1 in flight
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (t + 2 < total) issue(t + 2);  // into the slot of stage t, taken as consumed
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  sink[(size_t)blockIdx.x * 512 + threadIdx.x] = (float)ring[(threadIdx.x * 131) & 131071];
+}
+
 // value i of the output: code i (E4M3, E5M2 or E2M1) converted to BF16 with the scale
 // 2^(scale_bytes[i / 32] - 127) passed to the conversion instruction as the float whose bits are
 // scale_byte << 23 (2^-127 as the denormal 0x00400000 for byte 0)
@@ -249,6 +297,26 @@ int moe_probe_hbm_read(const void* src, size_t bytes, int blocks, float* sink, v
   if (blocks < 1 || blocks > (1 << 20) || bytes % 16 || !src || !sink) return -1;
   probe_hbm_read_kernel<<<dim3(blocks), 256, 0, (hipStream_t)stream>>>(reinterpret_cast<const v4i_*>(src),
                                                                          (long long)(bytes / 16), sink);
+  return (int)hipGetLastError();
+}
+
+int moe_probe_dma_stream(const void* src, size_t src_bytes, int K, int blocks, int panels, int passes, int depth,
+                         float* sink, void* stream) {
+  if (!src || !sink || K < 128 || K > 65536 || K % 128 || blocks < 1 || blocks > 65536 || panels < 0 ||
+      panels > blocks || passes < 1 || passes > 65536 || (depth != 1 && depth != 2))
+    return -1;
+  if (src_bytes < (size_t)(panels ? panels : blocks) * 512 * (size_t)K) return -1;
+  const int lds = 2 * 65536;
+  hipError_t e = depth == 1 ? hipFuncSetAttribute((const void*)probe_dma_stream_kernel<1>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds)
+                            : hipFuncSetAttribute((const void*)probe_dma_stream_kernel<2>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return (int)e;
+  const uint8_t* s8 = reinterpret_cast<const uint8_t*>(src);
+  if (depth == 1)
+    probe_dma_stream_kernel<1><<<dim3(blocks), 512, lds, (hipStream_t)stream>>>(s8, K, panels, passes, sink);
+  else
+    probe_dma_stream_kernel<2><<<dim3(blocks), 512, lds, (hipStream_t)stream>>>(s8, K, panels, passes, sink);
   return (int)hipGetLastError();
 }
 

@@ -191,6 +191,14 @@ def test_probe_arguments_rejected_before_launch():
     assert lib.moe_probe_mfma_gemm(0, 1, 128, 0, None, fake, fake, None) == -1   # NULL operand
     assert lib.moe_probe_mfma_loop(0, 10, 0, fake, None) == -1
     assert lib.moe_probe_hbm_read(fake, 17, 1, fake, None) == -1                 # not whole 16-byte loads
+    lib.moe_probe_dma_stream.argtypes = [P, ctypes.c_size_t] + [ctypes.c_int] * 5 + [P, P]
+    one = 512 * 1024  # one panel of 512 rows of K = 1024 bytes
+    assert lib.moe_probe_dma_stream(fake, one, 1000, 1, 0, 1, 1, fake, None) == -1   # K not a multiple of 128
+    assert lib.moe_probe_dma_stream(fake, one, 1024, 2, 0, 1, 1, fake, None) == -1   # two panels, one in src
+    assert lib.moe_probe_dma_stream(fake, one, 1024, 2, 3, 1, 1, fake, None) == -1   # more panels than workgroups
+    assert lib.moe_probe_dma_stream(fake, one, 1024, 1, 0, 1, 3, fake, None) == -1   # depth 3
+    assert lib.moe_probe_dma_stream(fake, one, 1024, 1, 0, 0, 1, fake, None) == -1   # no pass
+    assert lib.moe_probe_dma_stream(fake, one, 1024, 1, 0, 1, 1, None, None) == -1   # no sink
 
 
 def test_static_scratch_entry_rejects_large_layers_before_launch(L):
