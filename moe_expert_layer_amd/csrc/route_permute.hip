@@ -500,9 +500,10 @@ __global__ __launch_bounds__(1024) void permute_tiny_kernel(const int32_t* __res
   }
 }
 
-// Stable scatter of one 4096-slot chunk for up to 63 local experts, without per-round
-// barriers: every wave ranks its slots of all 16 rounds by ballot matching (sub-chunk
-// 4 r + w holds the chunk's slots [256 r + 64 w, + 64), so sub-chunks are in slot order),
+// Stable scatter of one chunk (kPermChunk slots) for up to 63 local experts, without
+// per-round barriers: every wave ranks its slots of all kPermChunk / 256 rounds by ballot
+// matching (sub-chunk 4 r + w holds the chunk's slots [256 r + 64 w, + 64), so sub-chunks are
+// in slot order),
 // one wave per bucket turns the sub-chunk counts into exclusive prefixes, and each slot's
 // position is offset + the chunk's base + the prefix of its sub-chunk + its rank.
 __global__ __launch_bounds__(256) void permute_scatter64_kernel(const int32_t* __restrict__ ids, int nslots, int e0,
@@ -511,8 +512,8 @@ __global__ __launch_bounds__(256) void permute_scatter64_kernel(const int32_t* _
                                                                 int32_t* __restrict__ row_to_slot,
                                                                 int32_t* __restrict__ slot_to_row) {
   constexpr int kRounds = kPermChunk / 256;
-  constexpr int kSub = kRounds * 4;  // 64 sub-chunks of 64 slots
-  static_assert(kSub == 64, "one lane per sub-chunk in the prefix");
+  constexpr int kSub = kRounds * 4;  // sub-chunks of 64 slots (one per wave and round)
+  static_assert(kSub <= 64 && kPermChunk % 256 == 0, "one lane per sub-chunk in the prefix");
   __shared__ int sc[kPermTinyBuckets][kSub];  // [bucket][sub-chunk]: count, then prefix
   __shared__ int base[kPermTinyBuckets];
   const int NB = EL + 1;
@@ -547,8 +548,9 @@ __global__ __launch_bounds__(256) void permute_scatter64_kernel(const int32_t* _
   }
   __syncthreads();
   for (int b = wave; b < NB; b += 4) {
-    const int v = sc[b][lane];
-    sc[b][lane] = wave_inclusive_scan_dpp(v) - v;
+    const int v = lane < kSub ? sc[b][lane] : 0;
+    const int ex = wave_inclusive_scan_dpp(v) - v;
+    if (lane < kSub) sc[b][lane] = ex;
   }
   __syncthreads();
 #pragma unroll

@@ -5,7 +5,7 @@ prefixes over one or two wave-wide passes), the one-workgroup permute with a one
 bucket scan (more slots, at most 63 local experts) or the block scan (64 to 256 local
 experts), several rounds of 1024 slots, and the chunked multi-workgroup permute (more than
 16384 slots or more than 256 local experts; ballot-ranked chunks for at most 63 local
-experts, more than 64 chunks in one case)."""
+experts, over several wave-wide passes of the chunk scan)."""
 import numpy as np
 import pytest
 
@@ -29,7 +29,9 @@ CASES = [  # tokens, experts, local_begin, local, topk
     (2048, 64, 3, 40, 8),     # 16384 slots exactly: sixteen rounds
     (2049, 64, 3, 40, 8),     # one slot more: chunked permute
     (64, 1024, 500, 300, 16), # 301 buckets: chunked permute
-    (33000, 64, 3, 40, 8),    # 264000 slots = 65 chunks: the chunk scan carries into a second pass
+    (33000, 64, 3, 40, 8),    # 264000 slots = 258 chunks of 1024: the chunk scan carries over five passes
+    (8192, 64, 3, 40, 8),     # 65536 slots = 64 chunks exactly
+    (8193, 64, 3, 40, 8),     # 65 chunks, the last one of 8 slots
     # 16384 tokens or more: routing with one 16-lane row per token (1, 2 and 8 keys per lane)
     (16384, 16, 0, 16, 4),
     (16400, 32, 0, 20, 3),
