@@ -273,11 +273,11 @@ constexpr int kWgPerCu = NSTAGE * Cfg<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, P
 // free where the GEMM streams weights (few rows per expert).
 //
 // PT (FC2 only): persistent workgroups.  Each workgroup walks its XCD's tile range with a stride
-// of the workgroups on that XCD, and stores a tile's Y2 rows only after it has issued the next
-// tile's first DMA stages, so the store burst at the end of a tile overlaps the next tile's
-// operand loads instead of idling the matrix cores.  The tile plan then lives outside the
-// stage ring, and the stores precede the DMAs in issue order, so every stage wait (which counts
-// outstanding vector memory operations in issue order) also covers them.
+// of the workgroups on that XCD, derives the tile plan once, and stores a tile's Y2 rows in the
+// next tile's prologue (after its token rows and scales are set up, just before its first DMA
+// stages are issued) instead of at the end of its own K loop.  The tile plan then lives outside
+// the stage ring.  The stores precede the DMAs in issue order, so the first stage wait (vector
+// memory operations complete in issue order) also covers them.
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE, int XA, int PT>
 __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE>)) void grouped_gemm_kernel(
     GemmArgs g) {
