@@ -33,13 +33,15 @@
 // Y2 stores).
 //
 // Tiles: BM rows x BN weight rows (FC1: BN = 256 = 128 gate + the matching 128 up rows,
-// i.e. exactly one 1x128 requant block of h; FC2: BN output columns), in three variants:
-// 128 rows with 4 waves (2 x 2), 256 rows with 8 waves (4 x 2) and 32 rows with 4 waves
-// (1 x 4).  K advances BK bytes per stage through a ring of NSTAGE LDS stages filled by
-// direct global->LDS loads (global_load_lds_dwordx4): NSTAGE-1 stages are in flight while
-// one is consumed, and the loads take no registers.  The waits are explicit (s_waitcnt vmcnt +
-// s_barrier).  LDS rows are 16-byte-chunk XOR swizzled so the operand reads are bank
-// conflict free.  Workgroups map to tiles in an XCD-aware order (consecutive tiles of one
+// i.e. exactly one 1x128 requant block of h; FC2: BN output columns), in three variants
+// chosen per call (launch_variant_w below): 256 rows (8 waves of 64 x 128; MXFP4 FC1: 4 waves
+// of 128 x 128; FC2 on persistent workgroups), 128 rows (8 waves; FC2 128 columns wide) and
+// 32 rows (4 waves of 32 x 64, the decode tile; its FC1 may sum exactly through BF16 MFMAs on
+// operands converted in registers, XA).  K advances BK bytes per stage through a ring of
+// NSTAGE LDS stages filled by direct global->LDS loads (global_load_lds_dwordx4): NSTAGE-1
+// stages are in flight while one is consumed, and the loads take no registers.  The waits are
+// explicit (s_waitcnt vmcnt + s_barrier).  LDS rows are 16-byte-chunk XOR swizzled so the
+// operand reads are bank conflict free.  Workgroups map to tiles in an XCD-aware order (consecutive tiles of one
 // expert on one XCD, sharing its L2).  Waves whose rows all lie past an expert's last row
 // skip their MFMAs (decode-sized experts).
 #include <hip/hip_runtime.h>
