@@ -66,3 +66,44 @@ def test_static_scratch_rejects_a_layer_too_large():
         B.moe_layer_static(d, t, t, t, t, t, t, t, y)
     assert ei.value.status == B.MOE_ERR_WORKSPACE
     assert "static" in str(ei.value)
+
+
+def test_static_entry_replays_under_graph_capture():
+    """moe_layer_static captured in a HIP graph (the case it exists for: a caller that cannot
+    allocate) replays to the eager result every time, with an eager call of another layer
+    shape between the replays overwriting the shared static array."""
+    w = synth.shrink(synth.workload("oai"), tokens=240, hidden=512, inter=256, num_experts=16, local_begin=2,
+                     num_local=12, topk=4, seed=44, name="oai-graph")
+    other = synth.shrink(synth.workload("tiny"), tokens=300, hidden=768, inter=384, num_experts=8, num_local=8,
+                         topk=2, seed=45, name="tiny-between")
+    dev, dev_other = G.upload(synth.generate(w)), G.upload(synth.generate(other))
+    eager = _static_call(w, dev)
+    d = B.desc_from_workload(w)
+    T, k, EL = w.tokens, w.topk, w.num_local
+    y = torch.zeros((T, w.hidden), dtype=torch.int16, device="cuda")
+    ids, tw = G.i32(T, k), torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts, offsets, r2s, s2r = G.i32(EL), G.i32(EL + 1), G.i32(T * k), G.i32(T * k)
+
+    def call():
+        B.moe_layer_static(d, dev["logits"], dev["x"], dev["x_sf"], dev["w1"], dev["w1_sf"], dev["w2"], dev["w2_sf"],
+                           y, ids, tw, counts, offsets, r2s, s2r)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        y.zero_()
+        _static_call(other, dev_other)  # eager work through the same static array
+        g.replay()
+        torch.cuda.synchronize()
+        got = {"y_bf16": y.cpu().numpy().view(np.uint16), "topk_ids": ids.cpu().numpy(), "topk_w": tw.cpu().numpy(),
+               "counts": counts.cpu().numpy(), "offsets": offsets.cpu().numpy(), "row_to_slot": r2s.cpu().numpy(),
+               "slot_to_row": s2r.cpu().numpy()}
+        _same(got, eager)
+        G.say(f"[no-alloc] graph replay {i}: equal to the eager call bit for bit")
