@@ -100,6 +100,13 @@ __device__ __forceinline__ bf16x8 fp4_group_bf16(const v8i& v, int q, float sc) 
 constexpr int kGroupN = 8;     // n-tiles per group in the tile order
 constexpr int kMaxKSteps = 64; // K <= 8192 (scales of a tile are staged in LDS, one per 128-wide step)
 
+// The tile's activation scales sit in LDS as [row][128-wide K step] bytes.  A row takes whole
+// dwords, an odd number of them, so that the 32 rows a wave reads at once (one byte each) fall
+// in 32 different banks; with the bare K / 128 bytes (16 or 56: an even number of dwords) rows
+// 8 or 16 apart shared a bank.  The table is rounded up to whole 256-byte DMA instructions.
+__host__ __device__ constexpr int asf_row_bytes(int nk128) { return nk128 ? ((((nk128 + 3) >> 2) | 1) << 2) : 0; }
+__host__ __device__ constexpr int asf_table_bytes(int bm, int nk128) { return (bm * asf_row_bytes(nk128) + 255) & ~255; }
+
 struct GemmArgs {
   const uint8_t* A;      // FC1: x [T, K]; FC2: h [cap, K]
   const uint8_t* A_sf;   // [rows, K/128]
@@ -294,7 +301,8 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   uint8_t* ring = lds;
   uint8_t* s_asf = lds + NSTAGE * C::STAGE;
   const int nk128_ = C::BF16 ? 0 : g.K / 128;
-  uint8_t* s_bsf = s_asf + BM * nk128_;
+  const int asr = asf_row_bytes(nk128_);  // bytes per row of the activation-scale table
+  uint8_t* s_bsf = s_asf + asf_table_bytes(BM, nk128_);
   int* s_tok = reinterpret_cast<int*>(ring + NSTAGE * C::STAGE - BM * 4);  // prologue only
   float(*s_amax)[BM] = reinterpret_cast<float(*)[BM]>(ring + BM * 128);      // epilogue only
 
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
   // scans the offsets itself.  Either way the plan and the expert offsets are put in LDS
   // (inside the ring, which the prologue does not use yet) by loads that are all in flight
   // together, so the expert search below reads LDS instead of chaining dependent global loads
-  int* s_plan = PT ? reinterpret_cast<int*>(lds + ((NSTAGE * C::STAGE + (BM + 2) * nk128_ + 15) & ~15))
+  int* s_plan = PT ? reinterpret_cast<int*>(lds + ((NSTAGE * C::STAGE + asf_table_bytes(BM, nk128_) + 2 * nk128_ + 15) & ~15))
                    : reinterpret_cast<int*>(ring);  // [EL + S + 1]
   int* s_wsum = s_plan + kMaxExperts + 8;      // [NW]
   int* s_offs = s_wsum + 16;                   // [EL + 1]
@@ -404,28 +412,31 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     bsf_v = g.tensor ? 127 : bsf_e[(long long)br * nk128 + ks];
   }
   __syncthreads();
-  // activation scales of the tile rows in LDS as [row][k step]: moved by 4-byte DMA when a
-  // row is whole dwords (nk128 % 4 == 0), else by byte loads
+  // activation scales of the tile rows in LDS as [row][k step] (rows asr bytes apart): moved by
+  // 4-byte DMA when a row is whole dwords (nk128 % 4 == 0), else by byte loads
   const bool asf_packed = g.asf_am > 0;
   const uint8_t* asf_gbase = MODE == 1 || asf_packed ? g.A_sf : g.A_sf + (long long)row_begin * nk128;
-  const bool asf_dma = !C::BF16 && !g.tensor && (nk128 & 3) == 0 && ((BM * nk128) & 255) == 0;
-  constexpr int kAsfDma = (BM * kMaxKSteps / 256 + NW - 1) / NW;  // 64-lane DMAs per wave, at most
-  const int asf_n = BM * nk128 / 256;                               // 64-lane DMAs of the tile
+  const bool asf_dma = !C::BF16 && !g.tensor && (nk128 & 3) == 0;
+  constexpr int kAsfDma = (asf_table_bytes(BM, kMaxKSteps) / 256 + NW - 1) / NW;  // 64-lane DMAs per wave, at most
+  const int asf_n = asf_table_bytes(BM, nk128) / 256;                              // 64-lane DMAs of the tile
   uint32_t asf_off[kAsfDma];
   if (asf_dma) {
-    const int dpr = nk128 / 4;  // dwords per row
+    // lane q of the table's DMAs fills dword q: row q / spr, data dword q % spr of it; the pad
+    // dword of a row and the rows past the tile (the 256-byte rounding) repeat a valid dword
+    const int dpr = nk128 / 4, spr = asr / 4;  // data dwords and table dwords per row
 #pragma unroll
     for (int j = 0; j < kAsfDma; ++j) {
-      const int q = (wave + NW * j) * 64 + lane, row = min(q / dpr, BM - 1);
-      asf_off[j] = asf_packed ? ((uint32_t)(q - row * dpr) * (uint32_t)g.asf_am + (uint32_t)s_tok[row]) * 4u
+      const int q = (wave + NW * j) * 64 + lane, r0 = q / spr;
+      const int row = min(r0, BM - 1), dw = min(q - r0 * spr, dpr - 1);
+      asf_off[j] = asf_packed ? ((uint32_t)dw * (uint32_t)g.asf_am + (uint32_t)s_tok[row]) * 4u
                               : (uint32_t)(s_tok[row] - (MODE == 1 ? 0 : row_begin)) * (uint32_t)nk128 +
-                                    (uint32_t)(q - row * dpr) * 4u;
+                                    (uint32_t)dw * 4u;
     }
   } else if (!C::BF16) {
     for (int i = tid; i < nk128 * BM; i += C::NTHR) {
       const int r = i / nk128;
       const int ks = i - r * nk128;
-      s_asf[i] = g.tensor ? 127
+      s_asf[r * asr + ks] = g.tensor ? 127
                  : asf_packed ? asf_gbase[((long long)(ks >> 2) * g.asf_am + s_tok[r]) * 4 + (ks & 3)]
                               : asf_gbase[(long long)(s_tok[r] - (MODE == 1 ? 0 : row_begin)) * nk128 + ks];
     }
@@ -539,7 +550,7 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
     const int k128 = (ks * BK) / 128;
     if (!C::BF16) {
 #pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi) f.sa[mi] = s_asf[(ra + mi * 32) * nk128 + k128];
+      for (int mi = 0; mi < C::MI; ++mi) f.sa[mi] = s_asf[(ra + mi * 32) * asr + k128];
     }
     int sbu0 = 0, sbu1 = 0;
     if (WFMT != 1 && !C::BF16) {  // one weight scale per 128x128 block
@@ -914,8 +925,9 @@ static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   auto kern = grouped_gemm_kernel<MODE, WFMT, BM, BN, BK, NSTAGE, NW, WTM, PIPE, XA, PT>;
   constexpr size_t kPlanBytes = (2 * kMaxExperts + 32) * 4;  // persistent: plan, block sums, offsets
   const size_t nk128 = C::BF16 ? 0 : a.K / 128;
-  const size_t lds = PT ? (((size_t)NSTAGE * C::STAGE + (BM + 2) * nk128 + 15) & ~(size_t)15) + kPlanBytes
-                        : (size_t)NSTAGE * C::STAGE + (size_t)BM * (a.K / 128) + 2 * (a.K / 128);
+  const size_t tab = (size_t)asf_table_bytes(BM, (int)nk128) + 2 * nk128;  // activation and weight scales
+  const size_t lds = PT ? (((size_t)NSTAGE * C::STAGE + tab + 15) & ~(size_t)15) + kPlanBytes
+                        : (size_t)NSTAGE * C::STAGE + tab;
   // raise the kernel's dynamic LDS limit to its largest size (K = 8192) once per device
   static std::atomic<uint64_t> ready{0};
   int dev = 0;
@@ -923,7 +935,8 @@ static hipError_t launch_one(const GemmArgs& a, size_t grid, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(ready.load(std::memory_order_acquire) & bit)) {
-    const size_t most = (size_t)NSTAGE * C::STAGE + (size_t)(BM + 2) * kMaxKSteps + (PT ? 16 + kPlanBytes : 0);
+    const size_t most = (size_t)NSTAGE * C::STAGE + (size_t)asf_table_bytes(BM, kMaxKSteps) + 2 * kMaxKSteps +
+                        (PT ? 16 + kPlanBytes : 0);
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
     if (e != hipSuccess) return e;
     ready.fetch_or(bit, std::memory_order_acq_rel);
