@@ -143,8 +143,9 @@ struct GemmArgs {
 };
 
 // Tile shape: BM rows x BN weight rows, K advancing BK per stage through an NSTAGE ring,
-// NW waves arranged (BM/WTM) x WN, each wave WTM rows x BN/WN weight rows.  PIPE: the operand
-// fragments of stage ks+1 are read from LDS while the MFMAs of stage ks run.
+// NW waves arranged (BM/WTM) x WN, each wave WTM rows x BN/WN weight rows.  PIPE 0: a stage's
+// fragments are read, then multiplied; PIPE 2: the half-step pipeline (the fragments of the
+// next 64-wide half of a stage are read from LDS while the MFMAs of the current half run).
 template <int MODE, int WFMT, int BM, int BN, int BK, int NSTAGE, int NW, int WTM, int PIPE>
 struct Cfg {
   static constexpr int NTHR = NW * 64;
@@ -175,7 +176,7 @@ struct Cfg {
   static_assert(A_INSTR >= 1 && B_DMA >= 1 && B_DMA * NW * 1024 == B_BYTES, "");
   static_assert(A_INSTR >= NW ? A_DMA * NW == A_INSTR : NW % A_INSTR == 0, "");
   static_assert(WFMT != 1 || BN <= NW * 64, "one scale DMA per wave covers 64 weight rows");
-  static_assert(PIPE != 1 || NSTAGE >= 3, "stage-ahead fragments need the next stage resident");
+  static_assert(PIPE == 0 || PIPE == 2, "stage-at-a-time or half-step pipeline");
   static_assert(PIPE != 2 || BK == 128, "the half-step pipeline splits 128-wide stages");
 };
 
@@ -669,23 +670,6 @@ __global__ __launch_bounds__(NW * 64, (kWgPerCu<MODE, WFMT, BM, BN, BK, NSTAGE, 
       F f;
       load_into(ks, 0, f);
       mma(f);
-    }
-  } else if (PIPE == 1) {
-    // stage ks+1 must be resident while stage ks multiplies: one stage less of DMA lookahead
-    F f0, f1;
-    wait_stages(min(nk - 1, NSTAGE - 2));
-    if (wave_live) load_into(0, 0, f0);
-    auto step = [&](int ks, F& cur, F& nxt) {
-      if (ks + 1 < nk) {
-        wait_stages(min(nk - 2 - ks, NSTAGE - 3));
-        if (ks + NSTAGE - 1 < nk) issue(ks + NSTAGE - 1);
-        if (wave_live) load_into(ks + 1, 0, nxt);
-      }
-      if (wave_live) mma(cur);
-    };
-    for (int ks = 0; ks < nk; ks += 2) {
-      step(ks, f0, f1);
-      if (ks + 1 < nk) step(ks + 1, f1, f0);
     }
   } else {
     // half-step pipeline (two 64-wide K steps per stage): the fragments of the next half are
